@@ -1,0 +1,507 @@
+"""Plain fp64 CPU oracle for Flex-Flash-Attention (FFA) over AttnSlices.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the library imports this module; only the
+tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` use
+it.  It shares no code with the HIP path.
+
+What it follows (MagiAttention pages):
+  * AttnSlice = (QRange, KRange, MaskType), a contiguous 2-D QK sub-mask; mask
+    types FULL, CAUSAL, INV-CAUSAL, BI-CAUSAL are named but not defined (blog
+    deep-dive, section "Flex-Flash-Attention 与 AttnSlice", AttnSlice equation).
+  * Mask semantics fixed by the build contract: CAUSAL is bottom-right aligned,
+    INV-CAUSAL top-left aligned, BI-CAUSAL their intersection; slices disjoint;
+    an empty row gives O = 0 and LSE = -inf.
+  * MaskArea: full = L^2, causal = L(L+1)/2, and FLOPs_fwd = 2*2*area*b*Hq*d,
+    FLOPs_bwd = 2.5*FLOPs_fwd (blog deep-dive, section "训练和 Benchmark 设置",
+    FLOPs equation and the area sentence after it).
+  * Block classes Full / Partial / Empty, q2k for forward and k2q for backward,
+    blocks out of bounds only in q counted as Full, CSR offsets
+    full_block_offset / mask_block_offset (documentation page, "FFA_FA4"
+    optimisations list, items 1 and 2).
+
+Readings where the pages are silent (each listed in the design notes):
+  ranges half-open; softmax scale default 1/sqrt(d); natural-log LSE including
+  the scale; GQA head h uses kv head h // (Hq/Hkv); k2q mirrors the q2k
+  out-of-bounds rule with the axes swapped; CSR lists ascending, Full and
+  Partial kept apart.
+
+Everything is float64 (bf16 inputs upcast exactly).  The forward is two-pass
+(LSE first, then O), unlike the GPU's online softmax.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Sequence, Tuple
+
+import numpy as np
+
+FULL, CAUSAL, INV_CAUSAL, BI_CAUSAL = 0, 1, 2, 3
+
+# status flags for a slice table (bitwise OR, same meaning as the library's
+# device status word)
+ERR_BOUNDS, ERR_TYPE, ERR_OVERLAP = 1, 2, 4
+
+
+def _as_f64(x) -> np.ndarray:
+    """torch tensor (any float dtype, CPU) or ndarray -> float64 ndarray (exact upcast)."""
+    if hasattr(x, "detach"):
+        x = x.detach().to("cpu")
+        import torch  # local: the oracle itself needs torch only to read tensors
+        return x.to(torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# c.2  the mask predicate (definition) and the row / column interval forms
+# ---------------------------------------------------------------------------
+
+def valid(i: int, j: int, s) -> bool:
+    """Is (query i, key j) in slice s?  The defining predicate.
+
+    r = i - q0, c = j - k0, Lq = q1 - q0, Lk = k1 - k0;
+      FULL:        inside the rectangle
+      CAUSAL:      c <= r + (Lk - Lq)     (bottom-right aligned diagonal)
+      INV_CAUSAL:  c >= r                 (top-left aligned diagonal)
+      BI_CAUSAL:   both
+    """
+    q0, q1, k0, k1, t = s
+    if not (q0 <= i < q1 and k0 <= j < k1):
+        return False
+    r, c, Lq, Lk = i - q0, j - k0, q1 - q0, k1 - k0
+    if t == FULL:
+        return True
+    if t == CAUSAL:
+        return c <= r + (Lk - Lq)
+    if t == INV_CAUSAL:
+        return c >= r
+    if t == BI_CAUSAL:
+        return c <= r + (Lk - Lq) and c >= r
+    raise ValueError(f"unknown mask type {t}")
+
+
+def dense_mask(slices: Sequence, Tq: int, Tk: int) -> np.ndarray:
+    """Materialised [Tq, Tk] int count of slices containing each (i, j), from the
+    predicate evaluated on the whole grid (brute force; small inputs only).
+    Disjoint tables give a 0/1 array."""
+    ii = np.arange(Tq)[:, None]
+    jj = np.arange(Tk)[None, :]
+    cnt = np.zeros((Tq, Tk), dtype=np.int64)
+    for (q0, q1, k0, k1, t) in slices:
+        inside = (ii >= q0) & (ii < q1) & (jj >= k0) & (jj < k1)
+        r, c, Lq, Lk = ii - q0, jj - k0, q1 - q0, k1 - k0
+        if t == FULL:
+            m = inside
+        elif t == CAUSAL:
+            m = inside & (c <= r + (Lk - Lq))
+        elif t == INV_CAUSAL:
+            m = inside & (c >= r)
+        elif t == BI_CAUSAL:
+            m = inside & (c <= r + (Lk - Lq)) & (c >= r)
+        else:
+            raise ValueError(t)
+        cnt += m
+    return cnt
+
+
+def row_interval(s, i: int):
+    """Keys valid for query i in slice s as an inclusive interval (lo, hi), or
+    None.  Solving the predicate for c at fixed r gives
+    c in [ (r if type in {INV,BI} else 0),  (min(Lk-1, r+Lk-Lq) if type in {CAUSAL,BI} else Lk-1) ]."""
+    q0, q1, k0, k1, t = s
+    if not (q0 <= i < q1) or k1 <= k0:
+        return None
+    r, Lq, Lk = i - q0, q1 - q0, k1 - k0
+    lo = r if t in (INV_CAUSAL, BI_CAUSAL) else 0
+    hi = min(Lk - 1, r + Lk - Lq) if t in (CAUSAL, BI_CAUSAL) else Lk - 1
+    if lo > hi:
+        return None
+    return (k0 + lo, k0 + hi)
+
+
+def col_interval(s, j: int):
+    """Queries valid for key j in slice s as an inclusive interval, or None.
+    Solving the predicate for r at fixed c: CAUSAL needs r >= c - (Lk-Lq),
+    INV_CAUSAL needs r <= c."""
+    q0, q1, k0, k1, t = s
+    if not (k0 <= j < k1) or q1 <= q0:
+        return None
+    c, Lq, Lk = j - k0, q1 - q0, k1 - k0
+    lo = max(0, c - (Lk - Lq)) if t in (CAUSAL, BI_CAUSAL) else 0
+    hi = min(Lq - 1, c) if t in (INV_CAUSAL, BI_CAUSAL) else Lq - 1
+    if lo > hi:
+        return None
+    return (q0 + lo, q0 + hi)
+
+
+def row_intervals_vec(s, rows: np.ndarray):
+    """Vectorised ``row_interval`` over an int array of rows: (lo, hi, ok)."""
+    q0, q1, k0, k1, t = s
+    rows = np.asarray(rows, dtype=np.int64)
+    r, Lq, Lk = rows - q0, q1 - q0, k1 - k0
+    lo = r if t in (INV_CAUSAL, BI_CAUSAL) else np.zeros_like(r)
+    hi = np.minimum(Lk - 1, r + Lk - Lq) if t in (CAUSAL, BI_CAUSAL) else np.full_like(r, Lk - 1)
+    ok = (rows >= q0) & (rows < q1) & (lo <= hi) & (Lk > 0)
+    return k0 + lo, k0 + hi, ok
+
+
+def valid_keys(slices: Sequence, i: int) -> np.ndarray:
+    """Sorted array J_i of keys valid for query i (union over slices)."""
+    parts = []
+    for s in slices:
+        iv = row_interval(s, i)
+        if iv is not None:
+            parts.append(np.arange(iv[0], iv[1] + 1))
+    if not parts:
+        return np.zeros(0, dtype=np.int64)
+    return np.unique(np.concatenate(parts))
+
+
+# ---------------------------------------------------------------------------
+# c.3  areas and FLOPs
+# ---------------------------------------------------------------------------
+
+def slice_area(s) -> int:
+    """Number of valid (i, j) in one slice, closed form per mask type.
+
+    FULL: Lq*Lk.  CAUSAL and INV_CAUSAL: Lq*Lk - Lq(Lq-1)/2 if Lk >= Lq, else
+    Lk(Lk+1)/2.  BI_CAUSAL: Lq(Lk-Lq+1) if Lk >= Lq, else 0.  With Lq = Lk = L
+    these are the pages' L^2 and L(L+1)/2."""
+    q0, q1, k0, k1, t = s
+    Lq, Lk = max(0, q1 - q0), max(0, k1 - k0)
+    if Lq == 0 or Lk == 0:
+        return 0
+    if t == FULL:
+        return Lq * Lk
+    if t in (CAUSAL, INV_CAUSAL):
+        return Lq * Lk - Lq * (Lq - 1) // 2 if Lk >= Lq else Lk * (Lk + 1) // 2
+    if t == BI_CAUSAL:
+        return Lq * (Lk - Lq + 1) if Lk >= Lq else 0
+    raise ValueError(t)
+
+
+def total_area(slices: Sequence) -> int:
+    """Valid-mask area of a disjoint slice table: the sum of slice areas."""
+    return sum(slice_area(s) for s in slices)
+
+
+def flops(area: int, num_heads_q: int, head_dim: int, batch: int = 1) -> Tuple[int, float]:
+    """(FLOPs_fwd, FLOPs_bwd) = (2*2*area*batch*Hq*d, 2.5 * FLOPs_fwd)."""
+    f = 2 * 2 * area * batch * num_heads_q * head_dim
+    return f, 2.5 * f
+
+
+# ---------------------------------------------------------------------------
+# slice-table validation
+# ---------------------------------------------------------------------------
+
+def validate(slices: Sequence, Tq: int, Tk: int) -> int:
+    """Bit flags: ERR_BOUNDS (a range outside [0,T] or start > end), ERR_TYPE
+    (mask type not 0..3), ERR_OVERLAP (two slices share a valid (i, j))."""
+    flags = 0
+    good = []
+    for s in slices:
+        q0, q1, k0, k1, t = s
+        if not (0 <= q0 <= q1 <= Tq and 0 <= k0 <= k1 <= Tk):
+            flags |= ERR_BOUNDS
+            continue
+        if t not in (FULL, CAUSAL, INV_CAUSAL, BI_CAUSAL):
+            flags |= ERR_TYPE
+            continue
+        good.append(s)
+    # overlap: some row has intersecting intervals from two slices
+    for a in range(len(good)):
+        for b in range(a + 1, len(good)):
+            sa, sb = good[a], good[b]
+            r0, r1 = max(sa[0], sb[0]), min(sa[1], sb[1])
+            if r0 >= r1 or max(sa[2], sb[2]) >= min(sa[3], sb[3]):
+                continue
+            rows = np.arange(r0, r1)
+            la, ha, oka = row_intervals_vec(sa, rows)
+            lb, hb, okb = row_intervals_vec(sb, rows)
+            if np.any(oka & okb & (np.maximum(la, lb) <= np.minimum(ha, hb))):
+                flags |= ERR_OVERLAP
+    return flags
+
+
+# ---------------------------------------------------------------------------
+# c.6  block metadata
+# ---------------------------------------------------------------------------
+
+def tile_counts_dense(slices: Sequence, Tq: int, Tk: int, BM: int, BN: int) -> np.ndarray:
+    """v[m, n] = number of valid (i, j) in tile rows [m*BM, (m+1)*BM) x cols
+    [n*BN, (n+1)*BN), counted on the materialised mask (brute force)."""
+    mask = dense_mask(slices, Tq, Tk)
+    nm, nn = -(-Tq // BM), -(-Tk // BN)
+    pad = np.zeros((nm * BM, nn * BN), dtype=np.int64)
+    pad[:Tq, :Tk] = mask
+    return pad.reshape(nm, BM, nn, BN).sum(axis=(1, 3))
+
+
+def tile_counts(slices: Sequence, Tq: int, Tk: int, BM: int, BN: int) -> Dict[int, np.ndarray]:
+    """Same counts without materialising the mask, for large tables.
+
+    For one q-block, every valid pair lies in some row's interval.  Let
+    H(x) = number of valid pairs in the block with key < x
+         = sum over intervals [lo, hi] of clip(x - lo, 0, hi - lo + 1).
+    Then v[m, n] = H((n+1)*BN) - H(n*BN).  Returns {m: int64 array over n} for
+    q-blocks that contain any valid pair."""
+    nm, nn = -(-Tq // BM), -(-Tk // BN)
+    per_block: Dict[int, List[Tuple[np.ndarray, np.ndarray]]] = {}
+    for s in slices:
+        q0, q1 = s[0], s[1]
+        if q1 <= q0:
+            continue
+        for m in range(q0 // BM, (q1 - 1) // BM + 1):
+            rows = np.arange(max(q0, m * BM), min(q1, (m + 1) * BM))
+            lo, hi, ok = row_intervals_vec(s, rows)
+            if ok.any():
+                per_block.setdefault(m, []).append((lo[ok], hi[ok]))
+    out: Dict[int, np.ndarray] = {}
+    grid = np.arange(nn + 1, dtype=np.int64) * BN
+    for m, parts in per_block.items():
+        lo = np.concatenate([p[0] for p in parts])
+        hi = np.concatenate([p[1] for p in parts])
+        ln = hi - lo + 1
+        # H(x) = sum_{lo < x} (x - lo) - sum_{hi+1 < x} (x - hi - 1)
+        order_lo = np.sort(lo)
+        order_end = np.sort(hi + 1)
+        c_lo = np.concatenate([[0], np.cumsum(order_lo)])
+        c_end = np.concatenate([[0], np.cumsum(order_end)])
+        n_lo = np.searchsorted(order_lo, grid, side="left")     # lo < x
+        n_end = np.searchsorted(order_end, grid, side="left")   # hi+1 < x
+        H = (n_lo * grid - c_lo[n_lo]) - (n_end * grid - c_end[n_end])
+        v = np.diff(H)
+        assert v.sum() == ln.sum()
+        out[m] = v
+    return out
+
+
+def block_meta(slices: Sequence, Tq: int, Tk: int, BM: int, BN: int, direction: str,
+               dense: bool = False) -> dict:
+    """CSR block metadata.
+
+    Tiles are rows [m*BM, (m+1)*BM) x cols [n*BN, (n+1)*BN); v = valid count.
+      q2k (forward):  rows past Tq are ignored; cols past Tk count as invalid.
+                      Full iff v == rows_in_bounds(m) * BN.
+      k2q (backward): mirror - cols past Tk ignored, rows past Tq invalid.
+                      Full iff v == BM * cols_in_bounds(n).
+      Empty iff v == 0, else Partial.
+    q2k lists, per q-block m, ascending k-block indices; k2q lists, per k-block
+    n, ascending q-block indices.  Returns full_block_offset, full_block_idx,
+    mask_block_offset, mask_block_idx (int64 arrays) and the total area."""
+    nm, nn = -(-Tq // BM), -(-Tk // BN)
+    if dense:
+        V = tile_counts_dense(slices, Tq, Tk, BM, BN)
+        rows_v = {m: V[m] for m in range(nm) if V[m].any()}
+    else:
+        rows_v = tile_counts(slices, Tq, Tk, BM, BN)
+    area = int(sum(int(v.sum()) for v in rows_v.values()))
+    if direction == "q2k":
+        full_lists: List[List[int]] = [[] for _ in range(nm)]
+        mask_lists: List[List[int]] = [[] for _ in range(nm)]
+        for m, v in rows_v.items():
+            cap = (min((m + 1) * BM, Tq) - m * BM) * BN
+            nz = np.nonzero(v)[0]
+            full_lists[m] = [int(n) for n in nz if v[n] == cap]
+            mask_lists[m] = [int(n) for n in nz if v[n] != cap]
+    elif direction == "k2q":
+        full_lists = [[] for _ in range(nn)]
+        mask_lists = [[] for _ in range(nn)]
+        for m in sorted(rows_v):
+            v = rows_v[m]
+            for n in np.nonzero(v)[0]:
+                cap = BM * (min((n + 1) * BN, Tk) - n * BN)
+                (full_lists if v[n] == cap else mask_lists)[int(n)].append(m)
+    else:
+        raise ValueError(direction)
+
+    def csr(lists):
+        off = np.zeros(len(lists) + 1, dtype=np.int64)
+        off[1:] = np.cumsum([len(x) for x in lists])
+        idx = np.array([i for x in lists for i in x], dtype=np.int64)
+        return off, idx
+
+    fo, fi = csr(full_lists)
+    mo, mi = csr(mask_lists)
+    return {"full_block_offset": fo, "full_block_idx": fi,
+            "mask_block_offset": mo, "mask_block_idx": mi, "area": area}
+
+
+# ---------------------------------------------------------------------------
+# c.4 / c.5  attention forward and backward
+# ---------------------------------------------------------------------------
+
+def _row_batches(rows: np.ndarray, slices: Sequence, max_elems: int):
+    """Split sorted rows into batches; for each batch give the key window
+    [w0, w1) that contains every valid key of every row in it and the (rows x
+    window) validity mask built from the row intervals.  Rows are independent
+    and keys outside the window are invalid for all rows of the batch, so
+    attention over the window equals attention over all keys."""
+    lo_all = np.full(len(rows), np.iinfo(np.int64).max, dtype=np.int64)
+    hi_all = np.full(len(rows), -1, dtype=np.int64)
+    ivs = []
+    for s in slices:
+        lo, hi, ok = row_intervals_vec(s, rows)
+        if ok.any():
+            ivs.append((lo, hi, ok))
+            lo_all = np.where(ok, np.minimum(lo_all, lo), lo_all)
+            hi_all = np.where(ok, np.maximum(hi_all, hi), hi_all)
+    a = 0
+    n = len(rows)
+    while a < n:
+        b = a + 1
+        w0 = lo_all[a] if hi_all[a] >= 0 else 0
+        w1 = hi_all[a] + 1 if hi_all[a] >= 0 else 0
+        while b < n:
+            if hi_all[b] < 0:
+                nw0, nw1 = w0, w1
+            elif w1 <= w0:
+                nw0, nw1 = lo_all[b], hi_all[b] + 1
+            else:
+                nw0, nw1 = min(w0, lo_all[b]), max(w1, hi_all[b] + 1)
+            if (b + 1 - a) * max(1, nw1 - nw0) > max_elems:
+                break
+            w0, w1 = nw0, nw1
+            b += 1
+        w0, w1 = int(w0), int(max(w0, w1))
+        cols = np.arange(w0, w1)[None, :]
+        mask = np.zeros((b - a, w1 - w0), dtype=bool)
+        for lo, hi, ok in ivs:
+            sel = ok[a:b, None]
+            mask |= sel & (cols >= lo[a:b, None]) & (cols <= hi[a:b, None])
+        yield a, b, w0, w1, mask
+        a = b
+
+
+def _kv_head(h: int, Hq: int, Hkv: int) -> int:
+    return h // (Hq // Hkv)
+
+
+def forward(q, k, v, slices: Sequence, scale: float = None, rows=None,
+            max_elems: int = 1 << 22):
+    """O and LSE for the given query rows (default: all).
+
+    For each head h and row i with valid key set J_i:
+      s_ij = scale * q_i . k_j;  LSE_i = ln sum_{j in J_i} exp(s_ij)  (via max);
+      O_i = sum_{j in J_i} exp(s_ij - LSE_i) v_j;
+      J_i empty -> O_i = 0, LSE_i = -inf.
+    Returns O [len(rows), Hq, d] and LSE [Hq, len(rows)] (float64)."""
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    Tq, Hq, d = q.shape
+    Hkv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    rows = np.arange(Tq) if rows is None else np.asarray(rows, dtype=np.int64)
+    O = np.zeros((len(rows), Hq, d))
+    L = np.full((Hq, len(rows)), -np.inf)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        _forward_batches(q, k, v, slices, scale, rows, max_elems, O, L)
+    return O, L
+
+
+def _forward_batches(q, k, v, slices, scale, rows, max_elems, O, L):
+    Hq, Hkv = q.shape[1], k.shape[1]
+    for a, b, w0, w1, mask in _row_batches(rows, slices, max_elems):
+        if w1 <= w0:
+            continue
+        nonempty = mask.any(axis=1)
+        for h in range(Hq):
+            g = _kv_head(h, Hq, Hkv)
+            S = scale * (q[rows[a:b], h, :] @ k[w0:w1, g, :].T)
+            S = np.where(mask, S, -np.inf)
+            m = np.where(nonempty, S.max(axis=1, initial=-np.inf), 0.0)
+            lse = m + np.log(np.exp(S - m[:, None]).sum(axis=1))      # pass 1
+            P = np.where(mask, np.exp(S - np.where(nonempty, lse, 0.0)[:, None]), 0.0)
+            O[a:b, h, :] = P @ v[w0:w1, g, :]                              # pass 2
+            L[h, a:b] = np.where(nonempty, lse, -np.inf)
+
+
+def backward(q, k, v, do, slices: Sequence, scale: float = None, max_elems: int = 1 << 22):
+    """dQ, dK, dV (float64), the textbook gradient of ``forward`` over all rows.
+
+      P_ij = exp(s_ij - LSE_i) on J_i (0 elsewhere);  D_i = dO_i . O_i;
+      dS_ij = P_ij (dO_i . v_j - D_i);
+      dQ_i = scale sum_j dS_ij k_j;  dK_j = scale sum_{h in group} sum_i dS_ij q_i;
+      dV_j = sum_{h in group} sum_i P_ij dO_i.
+    O and LSE are recomputed here in float64."""
+    q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
+    Tq, Hq, d = q.shape
+    Tk, Hkv = k.shape[0], k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    rows = np.arange(Tq)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        _backward_batches(q, k, v, do, slices, scale, rows, max_elems, dq, dk, dv)
+    return dq, dk, dv
+
+
+def _backward_batches(q, k, v, do, slices, scale, rows, max_elems, dq, dk, dv):
+    Hq, Hkv = q.shape[1], k.shape[1]
+    for a, b, w0, w1, mask in _row_batches(rows, slices, max_elems):
+        if w1 <= w0:
+            continue
+        nonempty = mask.any(axis=1)
+        for h in range(Hq):
+            g = _kv_head(h, Hq, Hkv)
+            Kw, Vw = k[w0:w1, g, :], v[w0:w1, g, :]
+            S = scale * (q[a:b, h, :] @ Kw.T)
+            Sm = np.where(mask, S, -np.inf)
+            m = np.where(nonempty, Sm.max(axis=1, initial=-np.inf), 0.0)
+            lse = m + np.log(np.exp(Sm - m[:, None]).sum(axis=1))
+            P = np.where(mask, np.exp(S - np.where(nonempty, lse, 0.0)[:, None]), 0.0)
+            O = P @ Vw
+            D = (do[a:b, h, :] * O).sum(axis=1)
+            dP = do[a:b, h, :] @ Vw.T
+            dS = P * (dP - D[:, None])
+            dq[a:b, h, :] = scale * (dS @ Kw)
+            dk[w0:w1, g, :] += scale * (dS.T @ q[a:b, h, :])
+            dv[w0:w1, g, :] += P.T @ do[a:b, h, :]
+
+
+def backward_dq_rows(q, k, v, do, slices: Sequence, rows, scale: float = None,
+                     max_elems: int = 1 << 22):
+    """dQ for the given rows only (each row needs only its own O_i and LSE_i)."""
+    q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
+    Tq, Hq, d = q.shape
+    Hkv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.zeros((len(rows), Hq, d))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        _dq_batches(q, k, v, do, slices, scale, rows, max_elems, out)
+    return out
+
+
+def _dq_batches(q, k, v, do, slices, scale, rows, max_elems, out):
+    Hq, Hkv = q.shape[1], k.shape[1]
+    for a, b, w0, w1, mask in _row_batches(rows, slices, max_elems):
+        if w1 <= w0:
+            continue
+        nonempty = mask.any(axis=1)
+        for h in range(Hq):
+            g = _kv_head(h, Hq, Hkv)
+            Kw, Vw = k[w0:w1, g, :], v[w0:w1, g, :]
+            S = scale * (q[rows[a:b], h, :] @ Kw.T)
+            Sm = np.where(mask, S, -np.inf)
+            m = np.where(nonempty, Sm.max(axis=1, initial=-np.inf), 0.0)
+            lse = m + np.log(np.exp(Sm - m[:, None]).sum(axis=1))
+            P = np.where(mask, np.exp(S - np.where(nonempty, lse, 0.0)[:, None]), 0.0)
+            O = P @ Vw
+            D = (do[rows[a:b], h, :] * O).sum(axis=1)
+            dS = P * (do[rows[a:b], h, :] @ Vw.T - D[:, None])
+            out[a:b, h, :] = scale * (dS @ Kw)
+
+
+def lse_merge(o1, lse1, o2, lse2):
+    """Merge two partial attentions over disjoint key sets (same rows):
+    LSE = logaddexp(LSE1, LSE2), O = e^{LSE1-LSE} O1 + e^{LSE2-LSE} O2.
+    o: [rows, H, d], lse: [H, rows]."""
+    lse = np.logaddexp(lse1, lse2)
+    safe = np.where(np.isfinite(lse), lse, 0.0)
+    w1 = np.where(np.isfinite(lse1), np.exp(lse1 - safe), 0.0).T[:, :, None]
+    w2 = np.where(np.isfinite(lse2), np.exp(lse2 - safe), 0.0).T[:, :, None]
+    return w1 * o1 + w2 * o2, lse
