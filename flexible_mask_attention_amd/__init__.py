@@ -1,0 +1,285 @@
+"""Flex-Flash-Attention for AMD Instinct MI355X: Python binding of libffa.
+
+Argument marshalling only: every step runs in the HIP kernels of ``libffa.so``
+(see ``include/ffa.h``).  PyTorch provides device memory and the stream.  If
+the library is missing this module raises on first use; there is no fallback.
+
+    meta = build_meta(slices, seqlen_q, seqlen_k, head_dim)   # once per mask
+    o, lse = fwd(q, k, v, meta)
+    dq, dk, dv = bwd(q, k, v, o, lse, do, meta)
+    o = ffa_attention(q, k, v, meta)                          # autograd
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libffa.so")
+
+FULL, CAUSAL, INV_CAUSAL, BI_CAUSAL = 0, 1, 2, 3
+META_ERR_BOUNDS, META_ERR_TYPE, META_ERR_OVERLAP, META_ERR_CAPACITY = 1, 2, 4, 8
+
+EXPORTED = (
+    "ffa_block_meta_workspace_size", "ffa_build_block_meta", "ffa_block_meta_view", "ffa_fwd",
+    "ffa_bwd_workspace_size", "ffa_bwd", "ffa_status_string", "ffa_abi_version",
+)
+
+
+class FFAError(RuntimeError):
+    pass
+
+
+class TensorIn(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("token_stride", ctypes.c_int64),
+                ("head_stride", ctypes.c_int64)]
+
+
+class TensorOut(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("token_stride", ctypes.c_int64),
+                ("head_stride", ctypes.c_int64)]
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("seqlen_q", ctypes.c_int32), ("seqlen_k", ctypes.c_int32),
+                ("num_heads_q", ctypes.c_int32), ("num_heads_kv", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("softmax_scale", ctypes.c_float)]
+
+
+class MetaView(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "bm_fwd", "bn_fwd", "bm_bwd", "bn_bwd", "num_qblocks_fwd", "num_kblocks_fwd",
+        "num_qblocks_bwd", "num_kblocks_bwd")] + [("header_bytes", ctypes.c_int64)] + [
+        (n, ctypes.c_void_p) for n in (
+            "status", "area", "full_block_offset", "mask_block_offset", "k2q_full_block_offset",
+            "k2q_mask_block_offset", "qblock_slice_offset", "schedule_fwd", "schedule_bwd",
+            "index_base", "list_offsets")]
+
+
+_lib_handle = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libffa.so (built in-tree by ``__graft_entry__.build()``)."""
+    global _lib_handle
+    if _lib_handle is not None:
+        return _lib_handle
+    if not os.path.exists(LIB_PATH):
+        raise FFAError(f"{LIB_PATH} is missing: build it with `python -m flexible_mask_attention_amd._build`")
+    L = ctypes.CDLL(LIB_PATH)
+    st, i32, i64, vp, sz = ctypes.c_int, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+    L.ffa_block_meta_workspace_size.argtypes = [i32, i32, i32, i32, vp, ctypes.POINTER(sz)]
+    L.ffa_block_meta_workspace_size.restype = st
+    L.ffa_build_block_meta.argtypes = [vp, i32, i32, i32, i32, vp, sz, vp]
+    L.ffa_build_block_meta.restype = st
+    L.ffa_block_meta_view.argtypes = [vp, i32, i32, i32, i32, ctypes.POINTER(MetaView)]
+    L.ffa_block_meta_view.restype = st
+    L.ffa_fwd.argtypes = [ctypes.POINTER(Shape), TensorIn, TensorIn, TensorIn, vp, TensorOut, vp, vp]
+    L.ffa_fwd.restype = st
+    L.ffa_bwd_workspace_size.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(sz)]
+    L.ffa_bwd_workspace_size.restype = st
+    L.ffa_bwd.argtypes = [ctypes.POINTER(Shape), TensorIn, TensorIn, TensorIn, TensorIn, vp, TensorIn,
+                          vp, TensorOut, TensorOut, TensorOut, vp, sz, vp]
+    L.ffa_bwd.restype = st
+    L.ffa_status_string.argtypes = [st]
+    L.ffa_status_string.restype = ctypes.c_char_p
+    L.ffa_abi_version.argtypes = []
+    L.ffa_abi_version.restype = i32
+    _lib_handle = L
+    return L
+
+
+def _check(code: int, what: str):
+    if code != 0:
+        raise FFAError(f"{what}: {lib().ffa_status_string(code).decode()} (status {code})")
+
+
+def _stream(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _tin(t: torch.Tensor) -> TensorIn:
+    return TensorIn(t.data_ptr(), t.stride(0), t.stride(1))
+
+
+def _tout(t: torch.Tensor) -> TensorOut:
+    return TensorOut(t.data_ptr(), t.stride(0), t.stride(1))
+
+
+def _check_thd(t: torch.Tensor, name: str):
+    if t.dtype != torch.bfloat16 or t.dim() != 3 or not t.is_cuda:
+        raise FFAError(f"{name} must be a 3-D bfloat16 CUDA tensor [tokens, heads, head_dim]")
+    if t.stride(2) != 1:
+        raise FFAError(f"{name}: the head_dim axis must be contiguous")
+
+
+class BlockMeta:
+    """Device block metadata of one slice table (q2k and k2q CSR lists)."""
+
+    def __init__(self, buf: torch.Tensor, num_slices: int, seqlen_q: int, seqlen_k: int, head_dim: int):
+        self.buf, self.num_slices = buf, num_slices
+        self.seqlen_q, self.seqlen_k, self.head_dim = seqlen_q, seqlen_k, head_dim
+        v = MetaView()
+        _check(lib().ffa_block_meta_view(buf.data_ptr(), num_slices, seqlen_q, seqlen_k, head_dim,
+                                         ctypes.byref(v)), "ffa_block_meta_view")
+        self.view = v
+
+    @property
+    def ptr(self) -> int:
+        return self.buf.data_ptr()
+
+    def _read(self, addr: int, n: int, dtype) -> torch.Tensor:
+        off = addr - self.buf.data_ptr()
+        item = torch.empty((), dtype=dtype).element_size()
+        return self.buf[off:off + n * item].view(dtype).cpu()
+
+    def status(self) -> int:
+        """Device status word (synchronising read)."""
+        return int(self._read(self.view.status, 1, torch.int32)[0])
+
+    def area(self) -> int:
+        """Exact number of valid (query, key) pairs (synchronising read)."""
+        return int(self._read(self.view.area, 1, torch.int64)[0])
+
+    def csr(self) -> dict:
+        """All CSR arrays as CPU int64 tensors (synchronising; for tests and tools)."""
+        v = self.view
+        nqf, nkb = v.num_qblocks_fwd, v.num_kblocks_bwd
+        lo = self._read(v.list_offsets, 5, torch.int64).tolist()
+        qf = self._read(v.full_block_offset, nqf + 1, torch.int32).long()
+        qm = self._read(v.mask_block_offset, nqf + 1, torch.int32).long()
+        kf = self._read(v.k2q_full_block_offset, nkb + 1, torch.int32).long()
+        km = self._read(v.k2q_mask_block_offset, nkb + 1, torch.int32).long()
+        qs = self._read(v.qblock_slice_offset, nqf + 1, torch.int32).long()
+        base = v.index_base
+
+        def lst(i, n):
+            return self._read(base + 4 * lo[i], n, torch.int32).long() if n else torch.zeros(0, dtype=torch.long)
+
+        return {
+            "q2k": {"full_block_offset": qf, "full_block_idx": lst(0, int(qf[-1])),
+                    "mask_block_offset": qm, "mask_block_idx": lst(1, int(qm[-1]))},
+            "k2q": {"full_block_offset": kf, "full_block_idx": lst(2, int(kf[-1])),
+                    "mask_block_offset": km, "mask_block_idx": lst(3, int(km[-1]))},
+            "qblock_slice_offset": qs, "qblock_slice_idx": lst(4, int(qs[-1])),
+            "schedule_fwd": self._read(v.schedule_fwd, nqf, torch.int32).long(),
+            "schedule_bwd": self._read(v.schedule_bwd, nkb, torch.int32).long(),
+            "tiles": (v.bm_fwd, v.bn_fwd, v.bm_bwd, v.bn_bwd),
+        }
+
+
+def meta_workspace_size(num_slices: int, seqlen_q: int, seqlen_k: int, head_dim: int,
+                        host_slices: Optional[torch.Tensor] = None) -> int:
+    n = ctypes.c_size_t()
+    hp = None
+    if host_slices is not None:
+        host_slices = host_slices.to(torch.int32).contiguous().cpu()
+        hp = host_slices.data_ptr()
+    _check(lib().ffa_block_meta_workspace_size(num_slices, seqlen_q, seqlen_k, head_dim, hp,
+                                               ctypes.byref(n)), "ffa_block_meta_workspace_size")
+    return n.value
+
+
+def build_meta(slices, seqlen_q: int, seqlen_k: int, head_dim: int, device=None,
+               stream=None, out: Optional[torch.Tensor] = None) -> BlockMeta:
+    """Build block metadata for a slice table.
+
+    ``slices``: sequence of (q_start, q_end, k_start, k_end, mask_type) or an
+    int32 tensor [S, 5] (host or device).  The buffer is sized from the host
+    copy of the table when one is available; ``out`` (uint8, 256-byte aligned)
+    is used as given, and the device status word reports a table that does
+    not fit in it."""
+    if isinstance(slices, torch.Tensor):
+        t = slices.to(torch.int32).reshape(-1, 5)
+    else:
+        t = torch.tensor([list(s) for s in slices], dtype=torch.int32).reshape(-1, 5)
+    host = t.cpu() if not t.is_cuda else None
+    dev = torch.device(device) if device is not None else (t.device if t.is_cuda else torch.device("cuda"))
+    d_slices = t.to(dev).contiguous()
+    S = d_slices.shape[0]
+    if out is None:
+        nbytes = meta_workspace_size(S, seqlen_q, seqlen_k, head_dim, host)
+        out = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    _check(lib().ffa_build_block_meta(d_slices.data_ptr() if S else None, S, seqlen_q, seqlen_k, head_dim,
+                                      out.data_ptr(), out.numel(), _stream(stream)), "ffa_build_block_meta")
+    m = BlockMeta(out, S, seqlen_q, seqlen_k, head_dim)
+    m._slices = d_slices      # keep the device table alive with the metadata
+    return m
+
+
+def _shape(q, k, scale) -> Shape:
+    Tq, Hq, d = q.shape
+    Tk, Hkv = k.shape[0], k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    return Shape(Tq, Tk, Hq, Hkv, d, float(scale))
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, meta: BlockMeta, scale: float = None,
+        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, stream=None):
+    """Forward.  q [Tq,Hq,d], k/v [Tk,Hkv,d] bf16 -> (o [Tq,Hq,d] bf16, lse [Hq,Tq] fp32)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check_thd(t, n)
+    sh = _shape(q, k, scale)
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if lse is None:
+        lse = torch.empty(q.shape[1], q.shape[0], dtype=torch.float32, device=q.device)
+    _check(lib().ffa_fwd(ctypes.byref(sh), _tin(q), _tin(k), _tin(v), meta.ptr, _tout(out),
+                         lse.data_ptr(), _stream(stream)), "ffa_fwd")
+    return out, lse
+
+
+def bwd_workspace_size(q, k, scale=None) -> int:
+    n = ctypes.c_size_t()
+    sh = _shape(q, k, scale)
+    _check(lib().ffa_bwd_workspace_size(ctypes.byref(sh), ctypes.byref(n)), "ffa_bwd_workspace_size")
+    return n.value
+
+
+def bwd(q, k, v, o, lse, do, meta: BlockMeta, scale: float = None, dq=None, dk=None, dv=None,
+        workspace: Optional[torch.Tensor] = None, stream=None):
+    """Backward -> (dq, dk, dv), bf16, same shapes as q, k, v."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        _check_thd(t, n)
+    sh = _shape(q, k, scale)
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+    need = bwd_workspace_size(q, k, scale)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check(lib().ffa_bwd(ctypes.byref(sh), _tin(q), _tin(k), _tin(v), _tin(o), lse.data_ptr(), _tin(do),
+                         meta.ptr, _tout(dq), _tout(dk), _tout(dv), workspace.data_ptr(),
+                         workspace.numel(), _stream(stream)), "ffa_bwd")
+    return dq, dk, dv
+
+
+class FFAFunction(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, meta, scale):
+        o, lse = fwd(q, k, v, meta, scale)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.meta, ctx.scale = meta, scale
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = bwd(q, k, v, o, lse, do.contiguous(), ctx.meta, ctx.scale)
+        return dq, dk, dv, None, None
+
+
+def ffa_attention(q, k, v, meta: BlockMeta, scale: float = None) -> torch.Tensor:
+    """Flex-Flash-Attention with autograd support."""
+    return FFAFunction.apply(q, k, v, meta, scale)
+
+
+__all__ = ["build_meta", "fwd", "bwd", "ffa_attention", "FFAFunction", "BlockMeta", "lib",
+           "meta_workspace_size", "bwd_workspace_size", "FFAError", "FULL", "CAUSAL", "INV_CAUSAL",
+           "BI_CAUSAL", "EXPORTED"]

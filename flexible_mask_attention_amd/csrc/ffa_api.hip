@@ -1,0 +1,242 @@
+// ffa_api.hip - host side of the libffa C ABI: argument validation, metadata
+// layout and kernel dispatch.  Nothing here allocates, synchronises or keeps
+// state; every call only enqueues kernels on the caller's stream.
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "ffa_internal.hpp"
+
+using namespace ffa;
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// q2k and k2q tile counts touched by one slice's bounding rectangle, plus the
+// forward query blocks it spans: an upper bound on its CSR entries.
+int64_t slice_bound(const int32_t* s, int32_t Tq, int32_t Tk) {
+  const int64_t q0 = s[0], q1 = s[1], k0 = s[2], k1 = s[3];
+  if (!(0 <= q0 && q0 < q1 && q1 <= Tq && 0 <= k0 && k0 < k1 && k1 <= Tk)) return 0;
+  auto span = [](int64_t a, int64_t b, int64_t B) { return (b - 1) / B - a / B + 1; };
+  return span(q0, q1, BM_F) * span(k0, k1, BN_F) + span(q0, q1, BM_B) * span(k0, k1, BN_B) +
+         span(q0, q1, BM_F);
+}
+
+int64_t capacity_bound(int32_t S, int32_t Tq, int32_t Tk, const int32_t* host_slices) {
+  const MetaLayout L = meta_layout(S, Tq, Tk);
+  const int64_t dense = (int64_t)L.nq_f * L.nk_f + (int64_t)L.nq_b * L.nk_b + (int64_t)L.nq_f * S;
+  if (!host_slices) return dense;
+  int64_t b = 0;
+  for (int32_t i = 0; i < S; ++i) b += slice_bound(host_slices + 5 * i, Tq, Tk);
+  return b < dense ? b : dense;
+}
+
+bool check_tensor(const void* p, int64_t ts, int64_t hs, int64_t T, int64_t H, int D) {
+  if (T == 0) return true;
+  if (!p || !aligned(p, 16)) return false;
+  if (ts < 0 || hs < 0 || ts % 8 || hs % 8) return false;
+  (void)H;
+  (void)D;
+  return true;
+}
+
+ffa_status check_shape(const ffa_shape* s) {
+  if (!s) return FFA_ERR_INVALID_ARGUMENT;
+  if (s->seqlen_q < 0 || s->seqlen_k < 0 || s->num_heads_q < 1 || s->num_heads_kv < 1)
+    return FFA_ERR_INVALID_ARGUMENT;
+  if (s->num_heads_q % s->num_heads_kv) return FFA_ERR_INVALID_ARGUMENT;
+  if (s->head_dim != 64 && s->head_dim != 128) return FFA_ERR_UNSUPPORTED;
+  if (!std::isfinite(s->softmax_scale) || s->softmax_scale == 0.f) return FFA_ERR_INVALID_ARGUMENT;
+  return FFA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+FFA_API int32_t ffa_abi_version(void) { return FFA_ABI_VERSION; }
+
+FFA_API const char* ffa_status_string(ffa_status s) {
+  switch (s) {
+    case FFA_OK: return "ok";
+    case FFA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case FFA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FFA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case FFA_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+FFA_API ffa_status ffa_block_meta_workspace_size(int32_t num_slices, int32_t seqlen_q,
+                                                 int32_t seqlen_k, int32_t head_dim,
+                                                 const int32_t* host_slices, size_t* bytes) {
+  if (!bytes || num_slices < 0 || seqlen_q < 0 || seqlen_k < 0) return FFA_ERR_INVALID_ARGUMENT;
+  if (head_dim != 64 && head_dim != 128) return FFA_ERR_UNSUPPORTED;
+  const MetaLayout L = meta_layout(num_slices, seqlen_q, seqlen_k);
+  const int64_t cap = capacity_bound(num_slices, seqlen_q, seqlen_k, host_slices);
+  *bytes = (size_t)(L.fixed_bytes + align256(4 * cap));
+  return FFA_OK;
+}
+
+FFA_API ffa_status ffa_build_block_meta(const int32_t* d_slices, int32_t num_slices,
+                                        int32_t seqlen_q, int32_t seqlen_k, int32_t head_dim,
+                                        void* d_meta, size_t meta_bytes, void* stream) {
+  if (num_slices < 0 || seqlen_q < 0 || seqlen_k < 0) return FFA_ERR_INVALID_ARGUMENT;
+  if (head_dim != 64 && head_dim != 128) return FFA_ERR_UNSUPPORTED;
+  if (!d_meta || !aligned(d_meta, 256)) return FFA_ERR_INVALID_ARGUMENT;
+  if (num_slices > 0 && (!d_slices || !aligned(d_slices, 4))) return FFA_ERR_INVALID_ARGUMENT;
+  const MetaLayout L = meta_layout(num_slices, seqlen_q, seqlen_k);
+  if ((int64_t)meta_bytes < L.fixed_bytes) return FFA_ERR_WORKSPACE_TOO_SMALL;
+  const int64_t capacity = ((int64_t)meta_bytes - L.fixed_bytes) / 4;
+  hipError_t e = launch_build_meta(d_slices, num_slices, seqlen_q, seqlen_k, head_dim, d_meta,
+                                   capacity, L, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FFA_OK : FFA_ERR_HIP;
+}
+
+FFA_API ffa_status ffa_block_meta_view(const void* d_meta, int32_t num_slices, int32_t seqlen_q,
+                                       int32_t seqlen_k, int32_t head_dim,
+                                       ffa_block_meta_view_t* out) {
+  if (!d_meta || !out || num_slices < 0 || seqlen_q < 0 || seqlen_k < 0)
+    return FFA_ERR_INVALID_ARGUMENT;
+  if (head_dim != 64 && head_dim != 128) return FFA_ERR_UNSUPPORTED;
+  const MetaLayout L = meta_layout(num_slices, seqlen_q, seqlen_k);
+  const char* b = reinterpret_cast<const char*>(d_meta);
+  std::memset(out, 0, sizeof(*out));
+  out->bm_fwd = BM_F;
+  out->bn_fwd = BN_F;
+  out->bm_bwd = BM_B;
+  out->bn_bwd = BN_B;
+  out->num_qblocks_fwd = L.nq_f;
+  out->num_kblocks_fwd = L.nk_f;
+  out->num_qblocks_bwd = L.nq_b;
+  out->num_kblocks_bwd = L.nk_b;
+  out->header_bytes = HEADER_BYTES;
+  out->status = reinterpret_cast<const int32_t*>(b + offsetof(MetaHeader, status));
+  out->area = reinterpret_cast<const int64_t*>(b + offsetof(MetaHeader, area));
+  out->list_offsets = reinterpret_cast<const int64_t*>(b + offsetof(MetaHeader, list_off));
+  out->full_block_offset = reinterpret_cast<const int32_t*>(b + L.byte_off[A_QF_OFF]);
+  out->mask_block_offset = reinterpret_cast<const int32_t*>(b + L.byte_off[A_QM_OFF]);
+  out->k2q_full_block_offset = reinterpret_cast<const int32_t*>(b + L.byte_off[A_KF_OFF]);
+  out->k2q_mask_block_offset = reinterpret_cast<const int32_t*>(b + L.byte_off[A_KM_OFF]);
+  out->qblock_slice_offset = reinterpret_cast<const int32_t*>(b + L.byte_off[A_QS_OFF]);
+  out->schedule_fwd = reinterpret_cast<const int32_t*>(b + L.byte_off[A_SCHED_F]);
+  out->schedule_bwd = reinterpret_cast<const int32_t*>(b + L.byte_off[A_SCHED_B]);
+  out->index_base = reinterpret_cast<const int32_t*>(b + L.byte_off[A_VAR]);
+  return FFA_OK;
+}
+
+FFA_API ffa_status ffa_fwd(const ffa_shape* shape, ffa_tensor_in q, ffa_tensor_in k,
+                           ffa_tensor_in v, const void* d_meta, ffa_tensor_out o, float* lse,
+                           void* stream) {
+  ffa_status st = check_shape(shape);
+  if (st != FFA_OK) return st;
+  const int D = shape->head_dim, Tq = shape->seqlen_q, Tk = shape->seqlen_k;
+  const int Hq = shape->num_heads_q, Hkv = shape->num_heads_kv;
+  if (!check_tensor(q.ptr, q.token_stride, q.head_stride, Tq, Hq, D) ||
+      !check_tensor(o.ptr, o.token_stride, o.head_stride, Tq, Hq, D) ||
+      !check_tensor(k.ptr, k.token_stride, k.head_stride, Tk, Hkv, D) ||
+      !check_tensor(v.ptr, v.token_stride, v.head_stride, Tk, Hkv, D))
+    return FFA_ERR_INVALID_ARGUMENT;
+  if (Tq > 0 && (!lse || !aligned(lse, 16))) return FFA_ERR_INVALID_ARGUMENT;
+  if (!d_meta || !aligned(d_meta, 256)) return FFA_ERR_INVALID_ARGUMENT;
+  if (Tq == 0) return FFA_OK;
+  const MetaLayout L = meta_layout(0, Tq, Tk);
+  FwdArgs a;
+  a.q = static_cast<const __bf16*>(q.ptr);
+  a.k = static_cast<const __bf16*>(k.ptr);
+  a.v = static_cast<const __bf16*>(v.ptr);
+  a.o = static_cast<__bf16*>(o.ptr);
+  a.lse = lse;
+  a.meta = d_meta;
+  a.q_ts = q.token_stride;
+  a.q_hs = q.head_stride;
+  a.k_ts = k.token_stride;
+  a.k_hs = k.head_stride;
+  a.v_ts = v.token_stride;
+  a.v_hs = v.head_stride;
+  a.o_ts = o.token_stride;
+  a.o_hs = o.head_stride;
+  a.Tq = Tq;
+  a.Tk = Tk;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.scale = shape->softmax_scale;
+  a.scale_log2 = shape->softmax_scale * LOG2E;
+  hipError_t e = launch_fwd(a, D, L.nq_f, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FFA_OK : FFA_ERR_HIP;
+}
+
+FFA_API ffa_status ffa_bwd_workspace_size(const ffa_shape* shape, size_t* bytes) {
+  ffa_status st = check_shape(shape);
+  if (st != FFA_OK) return st;
+  if (!bytes) return FFA_ERR_INVALID_ARGUMENT;
+  *bytes = (size_t)align256(4LL * shape->num_heads_q * shape->seqlen_q);
+  return FFA_OK;
+}
+
+FFA_API ffa_status ffa_bwd(const ffa_shape* shape, ffa_tensor_in q, ffa_tensor_in k,
+                           ffa_tensor_in v, ffa_tensor_in o, const float* lse,
+                           ffa_tensor_in dout, const void* d_meta, ffa_tensor_out dq,
+                           ffa_tensor_out dk, ffa_tensor_out dv, void* d_ws, size_t ws_bytes,
+                           void* stream) {
+  ffa_status st = check_shape(shape);
+  if (st != FFA_OK) return st;
+  const int D = shape->head_dim, Tq = shape->seqlen_q, Tk = shape->seqlen_k;
+  const int Hq = shape->num_heads_q, Hkv = shape->num_heads_kv;
+  if (!check_tensor(q.ptr, q.token_stride, q.head_stride, Tq, Hq, D) ||
+      !check_tensor(o.ptr, o.token_stride, o.head_stride, Tq, Hq, D) ||
+      !check_tensor(dout.ptr, dout.token_stride, dout.head_stride, Tq, Hq, D) ||
+      !check_tensor(dq.ptr, dq.token_stride, dq.head_stride, Tq, Hq, D) ||
+      !check_tensor(k.ptr, k.token_stride, k.head_stride, Tk, Hkv, D) ||
+      !check_tensor(v.ptr, v.token_stride, v.head_stride, Tk, Hkv, D) ||
+      !check_tensor(dk.ptr, dk.token_stride, dk.head_stride, Tk, Hkv, D) ||
+      !check_tensor(dv.ptr, dv.token_stride, dv.head_stride, Tk, Hkv, D))
+    return FFA_ERR_INVALID_ARGUMENT;
+  if (Tq > 0 && (!lse || !aligned(lse, 16))) return FFA_ERR_INVALID_ARGUMENT;
+  if (!d_meta || !aligned(d_meta, 256)) return FFA_ERR_INVALID_ARGUMENT;
+  size_t need = 0;
+  ffa_bwd_workspace_size(shape, &need);
+  if (need > 0 && (!d_ws || !aligned(d_ws, 256))) return FFA_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < need) return FFA_ERR_WORKSPACE_TOO_SMALL;
+  if (Tq == 0 && Tk == 0) return FFA_OK;
+  const MetaLayout L = meta_layout(0, Tq, Tk);
+  BwdArgs a;
+  a.q = static_cast<const __bf16*>(q.ptr);
+  a.k = static_cast<const __bf16*>(k.ptr);
+  a.v = static_cast<const __bf16*>(v.ptr);
+  a.o = static_cast<const __bf16*>(o.ptr);
+  a.dout = static_cast<const __bf16*>(dout.ptr);
+  a.lse = lse;
+  a.dvec = static_cast<float*>(d_ws);
+  a.dq = static_cast<__bf16*>(dq.ptr);
+  a.dk = static_cast<__bf16*>(dk.ptr);
+  a.dv = static_cast<__bf16*>(dv.ptr);
+  a.meta = d_meta;
+  a.q_ts = q.token_stride;
+  a.q_hs = q.head_stride;
+  a.k_ts = k.token_stride;
+  a.k_hs = k.head_stride;
+  a.v_ts = v.token_stride;
+  a.v_hs = v.head_stride;
+  a.o_ts = o.token_stride;
+  a.o_hs = o.head_stride;
+  a.do_ts = dout.token_stride;
+  a.do_hs = dout.head_stride;
+  a.dq_ts = dq.token_stride;
+  a.dq_hs = dq.head_stride;
+  a.dk_ts = dk.token_stride;
+  a.dk_hs = dk.head_stride;
+  a.dv_ts = dv.token_stride;
+  a.dv_hs = dv.head_stride;
+  a.Tq = Tq;
+  a.Tk = Tk;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.scale = shape->softmax_scale;
+  a.scale_log2 = shape->softmax_scale * LOG2E;
+  hipError_t e = launch_bwd(a, D, L.nq_f, L.nk_b, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FFA_OK : FFA_ERR_HIP;
+}
+
+}  // extern "C"

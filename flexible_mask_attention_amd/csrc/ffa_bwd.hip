@@ -1,0 +1,472 @@
+// ffa_bwd.hip - Flex-Flash-Attention backward on gfx950.
+//
+// The pages say FFA has a backward and that its partial results are merged
+// (blog deep-dive, section "Flex-Flash-Attention 与 AttnSlice", Fig. 5: slice
+// level parallelism with atomic reduction of partials).  This backward is the
+// textbook gradient of masked softmax attention written so that every output
+// element has one owner and a fixed summation order, hence bitwise
+// reproducible results without atomics:
+//
+//   bwd_pre : D_i = dO_i . O_i                          (fp32, [Hq][Tq])
+//   dkdv    : owner (kv head, 128-key block); loops over the query heads that
+//             share the kv head and the k2q tiles of the block, in list order:
+//             S = Q K^T, P = exp(S - LSE) (masked on Partial tiles),
+//             dV += P^T dO, dP = dO V^T, dS = P (dP - D), dK += dS^T Q
+//   dq      : owner (query head, 128-row block); loops over its q2k tiles:
+//             S^T, P^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T
+//
+// MFMA orientation: in dkdv each lane owns one key (S = Q K^T leaves keys on
+// lanes), so P and dS feed the dV^T / dK^T MFMAs as B operands and dO^T, Q^T
+// come from LDS through transposed reads.  dq mirrors the forward (lanes own
+// query rows).
+#include "ffa_internal.hpp"
+
+namespace ffa {
+
+namespace {
+
+constexpr int NT = 256;
+
+// D_i = sum_c dO_ic O_ic, one group of D/8 lanes per (token, head)
+template <int D>
+__global__ __launch_bounds__(NT) void ffa_bwd_pre_kernel(BwdArgs a) {
+  constexpr int G = D / 8;
+  const int64_t rh = ((int64_t)blockIdx.x * NT + threadIdx.x) / G;
+  const int part = threadIdx.x % G;
+  const bool ok = rh < (int64_t)a.Tq * a.Hq;
+  float acc = 0.f;
+  int i = 0, h = 0;
+  if (ok) {
+    i = (int)(rh / a.Hq);
+    h = (int)(rh % a.Hq);
+    const u32x4 o = *reinterpret_cast<const u32x4*>(a.o + (int64_t)i * a.o_ts + (int64_t)h * a.o_hs + 8 * part);
+    const u32x4 g = *reinterpret_cast<const u32x4*>(a.dout + (int64_t)i * a.do_ts + (int64_t)h * a.do_hs + 8 * part);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t ou = o[e], gu = g[e];
+      acc += __uint_as_float(ou << 16) * __uint_as_float(gu << 16);
+      acc += __uint_as_float(ou & 0xffff0000u) * __uint_as_float(gu & 0xffff0000u);
+    }
+  }
+#pragma unroll
+  for (int off = G / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, G);
+  if (ok && part == 0) a.dvec[(int64_t)h * a.Tq + i] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: owner (kv head, BN_B-key block), 4 waves x 32 keys.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(NT, 1) void ffa_bwd_dkdv_kernel(BwdArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int TILE_B = BM_B * D * 2;          // bytes of one Q or dO tile
+  constexpr int STAGE_B = 2 * TILE_B + 2 * BM_B * 4;
+  constexpr int NCH = D / 8;
+  constexpr int PERT = BM_B * NCH / NT;
+  constexpr int QB = BM_B / 32;                 // 32-row query blocks per tile
+  constexpr int MB = D / 32;
+  constexpr int KS = D / 16;
+
+  const MetaView mv = meta_view(a.meta);
+  const MetaHeader* hd = mv.hdr;
+  if (hd->status != 0 || hd->seqlen_q != a.Tq || hd->seqlen_k != a.Tk) return;
+
+  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  const int l32 = lane & 31, h32 = lane >> 5, t16 = lane & 15, g16 = lane >> 4;
+  const int kvh = blockIdx.x % a.Hkv;
+  const int n = mv.sched_b[blockIdx.x / a.Hkv];
+  const int key = n * BN_B + wid * 32 + l32;
+  const bool kok = key < a.Tk;
+  const int G = a.Hq / a.Hkv;
+
+  const int f0 = mv.kf_off[n], nF = mv.kf_off[n + 1] - f0;
+  const int p0 = mv.km_off[n], nP = mv.km_off[n + 1] - p0;
+  const int nT = nP + nF;
+  const int32_t* fidx = mv.var + hd->list_off[L_KF] + f0;
+  const int32_t* pidx = mv.var + hd->list_off[L_KM] + p0;
+
+  // K and V as B operands: lane holds K[key][16k + 8*h32 + e]
+  bf16x8 kop[KS], vop[KS];
+  {
+    const __bf16* kp = a.k + (int64_t)key * a.k_ts + (int64_t)kvh * a.k_hs + 8 * h32;
+    const __bf16* vp = a.v + (int64_t)key * a.v_ts + (int64_t)kvh * a.v_hs + 8 * h32;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      u32x4 u = kok ? *reinterpret_cast<const u32x4*>(kp + 16 * k) : u32x4{0, 0, 0, 0};
+      u32x4 w = kok ? *reinterpret_cast<const u32x4*>(vp + 16 * k) : u32x4{0, 0, 0, 0};
+      __builtin_memcpy(&kop[k], &u, 16);
+      __builtin_memcpy(&vop[k], &w, 16);
+    }
+  }
+
+  f32x16 dkacc[MB], dvacc[MB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    dkacc[i] = f32x16{};
+    dvacc[i] = f32x16{};
+  }
+
+  u32x4 qreg[PERT], dreg[PERT];
+  float lreg = 0.f;   // threads 0..BM_B-1: lse*log2e of one row, BM_B..2BM_B-1: D of one row
+  const int total = G * nT;
+  auto tile_of = [&](int t) { return t < nP ? pidx[t] : fidx[t - nP]; };
+  auto gload = [&](int u) {
+    const int hq = kvh * G + u / nT;
+    const int m = tile_of(u % nT);
+    const __bf16* qb = a.q + (int64_t)hq * a.q_hs;
+    const __bf16* gb = a.dout + (int64_t)hq * a.do_hs;
+#pragma unroll
+    for (int i = 0; i < PERT; ++i) {
+      const int idx = tid + NT * i, r = idx / NCH, c = idx % NCH;
+      const int row = m * BM_B + r;
+      if (row < a.Tq) {
+        qreg[i] = *reinterpret_cast<const u32x4*>(qb + (int64_t)row * a.q_ts + 8 * c);
+        dreg[i] = *reinterpret_cast<const u32x4*>(gb + (int64_t)row * a.do_ts + 8 * c);
+      } else {
+        qreg[i] = u32x4{0, 0, 0, 0};
+        dreg[i] = u32x4{0, 0, 0, 0};
+      }
+    }
+    if (tid < 2 * BM_B) {
+      const int row = m * BM_B + (tid % BM_B);
+      float x = 0.f;
+      if (row < a.Tq) {
+        if (tid < BM_B) {
+          const float l = a.lse[(int64_t)hq * a.Tq + row];
+          x = (l == -INFINITY) ? 0.f : l * LOG2E;
+        } else {
+          x = a.dvec[(int64_t)hq * a.Tq + row];
+        }
+      }
+      lreg = x;
+    }
+  };
+  auto lstore = [&](int stage) {
+    char* qt = smem + stage * STAGE_B;
+    char* gt = qt + TILE_B;
+    float* lt = reinterpret_cast<float*>(gt + TILE_B);
+#pragma unroll
+    for (int i = 0; i < PERT; ++i) {
+      const int idx = tid + NT * i, r = idx / NCH, c = idx % NCH;
+      *reinterpret_cast<u32x4*>(qt + lds_off<D>(r, c)) = qreg[i];
+      *reinterpret_cast<u32x4*>(gt + lds_off<D>(r, c)) = dreg[i];
+    }
+    if (tid < 2 * BM_B) lt[tid] = lreg;
+  };
+
+  if (total > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+
+  for (int u = 0; u < total; ++u) {
+    const int stage = u & 1;
+    const int t = u % nT;
+    const bool masked = t < nP;
+    const int m = tile_of(t);
+    const int hq = kvh * G + u / nT;
+    (void)hq;
+    if (u + 1 < total) gload(u + 1);
+    const char* qt = smem + stage * STAGE_B;
+    const char* gt = qt + TILE_B;
+    const float* lt = reinterpret_cast<const float*>(gt + TILE_B);
+
+    // S = Q K^T and dP = dO V^T; lane = key, registers = rows 32qb + 8(r/4) + 4*h32 + r%4
+    f32x16 sacc[QB], pacc[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      sacc[qb] = f32x16{};
+      pacc[qb] = f32x16{};
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        const bf16x8 qa = read_row_operand<D>(qt, 32 * qb + l32, 2 * k + h32);
+        sacc[qb] = mfma32(qa, kop[k], sacc[qb]);
+        const bf16x8 ga = read_row_operand<D>(gt, 32 * qb + l32, 2 * k + h32);
+        pacc[qb] = mfma32(ga, vop[k], pacc[qb]);
+      }
+    }
+
+    uint64_t mk = ~0ull;
+    if (masked) {
+      // valid rows of this key inside [m0, m0 + BM_B), from the slices of the
+      // enclosing forward query block
+      const int m0 = m * BM_B;
+      const int mf = m0 / BM_F;
+      const int s0 = mv.qs_off[mf], nS = mv.qs_off[mf + 1] - s0;
+      const int32_t* sidx = mv.var + hd->list_off[L_QS] + s0;
+      mk = 0;
+      for (int si = 0; si < nS; ++si) {
+        const Slice s = load_slice(mv.slices, sidx[si]);
+        int lo, hi;
+        col_interval(s, key, lo, hi);
+        lo = max(lo, m0);
+        hi = min(hi, m0 + BM_B - 1);
+        if (lo <= hi) mk |= bit_range(lo - m0, hi - m0);
+      }
+      mk >>= 4 * h32;
+    }
+
+    float p[QB][16], ds[QB][16];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const uint32_t w = static_cast<uint32_t>(mk >> (32 * qb));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = 32 * qb + 8 * j + 4 * h32;
+        const f32x4 lse4 = *reinterpret_cast<const f32x4*>(lt + row);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(lt + BM_B + row);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * j + i;
+          float pv = __builtin_amdgcn_exp2f(sacc[qb][r] * a.scale_log2 - lse4[i]);
+          if (masked && !((w >> (8 * j + i)) & 1u)) pv = 0.f;
+          p[qb][r] = pv;
+          ds[qb][r] = pv * (pacc[qb][r] - d4[i]);
+        }
+      }
+    }
+
+    // dV^T += dO^T P and dK^T += Q^T dS over 16-row chunks
+#pragma unroll
+    for (int c = 0; c < BM_B / 16; ++c) {
+      const int qb = c >> 1, c2 = c & 1;
+      const bf16x8 pb = pack_bf16x8(&p[qb][8 * c2]);
+      const bf16x8 sb = pack_bf16x8(&ds[qb][8 * c2]);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int r0 = 32 * qb + 16 * c2 + 4 * h32, cb = 32 * mb + 16 * (g16 & 1);
+        const bf16x8 ga = read_tr_operand<D>(gt, r0, cb, t16);
+        dvacc[mb] = mfma32(ga, pb, dvacc[mb]);
+        const bf16x8 qa = read_tr_operand<D>(qt, r0, cb, t16);
+        dkacc[mb] = mfma32(qa, sb, dkacc[mb]);
+      }
+    }
+
+    if (u + 1 < total) lstore(stage ^ 1);
+    __syncthreads();
+  }
+
+  if (kok) {
+    __bf16* kp = a.dk + (int64_t)key * a.dk_ts + (int64_t)kvh * a.dk_hs;
+    __bf16* vp = a.dv + (int64_t)key * a.dv_ts + (int64_t)kvh * a.dv_hs;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf16x4 wk, wv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          wk[i] = static_cast<__bf16>(dkacc[mb][4 * j + i] * a.scale);
+          wv[i] = static_cast<__bf16>(dvacc[mb][4 * j + i]);
+        }
+        *reinterpret_cast<bf16x4*>(kp + 32 * mb + 8 * j + 4 * h32) = wk;
+        *reinterpret_cast<bf16x4*>(vp + 32 * mb + 8 * j + 4 * h32) = wv;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: owner (query head, BM_F-row block), 4 waves x 32 rows, q2k tiles.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(NT, 1) void ffa_bwd_dq_kernel(BwdArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int TILE_B = BN_F * D * 2;
+  constexpr int NCH = D / 8;
+  constexpr int PERT = BN_F * NCH / NT;
+  constexpr int KB = BN_F / 32;
+  constexpr int MB = D / 32;
+  constexpr int KS = D / 16;
+
+  const MetaView mv = meta_view(a.meta);
+  const MetaHeader* hd = mv.hdr;
+  if (hd->status != 0 || hd->seqlen_q != a.Tq || hd->seqlen_k != a.Tk) return;
+
+  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  const int l32 = lane & 31, h32 = lane >> 5, t16 = lane & 15, g16 = lane >> 4;
+  const int head = blockIdx.x % a.Hq;
+  const int m = mv.sched_f[blockIdx.x / a.Hq];
+  const int kvh = head / (a.Hq / a.Hkv);
+  const int qrow = m * BM_F + wid * 32 + l32;
+  const bool qok = qrow < a.Tq;
+
+  const int f0 = mv.qf_off[m], nF = mv.qf_off[m + 1] - f0;
+  const int p0 = mv.qm_off[m], nP = mv.qm_off[m + 1] - p0;
+  const int nT = nP + nF;
+  const int32_t* fidx = mv.var + hd->list_off[L_QF] + f0;
+  const int32_t* pidx = mv.var + hd->list_off[L_QM] + p0;
+  const int s0 = mv.qs_off[m], nS = mv.qs_off[m + 1] - s0;
+  const int32_t* sidx = mv.var + hd->list_off[L_QS] + s0;
+
+  bf16x8 qop[KS], gop[KS];
+  {
+    const __bf16* qp = a.q + (int64_t)qrow * a.q_ts + (int64_t)head * a.q_hs + 8 * h32;
+    const __bf16* gp = a.dout + (int64_t)qrow * a.do_ts + (int64_t)head * a.do_hs + 8 * h32;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      u32x4 u = qok ? *reinterpret_cast<const u32x4*>(qp + 16 * k) : u32x4{0, 0, 0, 0};
+      u32x4 w = qok ? *reinterpret_cast<const u32x4*>(gp + 16 * k) : u32x4{0, 0, 0, 0};
+      __builtin_memcpy(&qop[k], &u, 16);
+      __builtin_memcpy(&gop[k], &w, 16);
+    }
+  }
+  float lse_l2 = 0.f, dval = 0.f;
+  if (qok) {
+    const float l = a.lse[(int64_t)head * a.Tq + qrow];
+    lse_l2 = (l == -INFINITY) ? 0.f : l * LOG2E;
+    dval = a.dvec[(int64_t)head * a.Tq + qrow];
+  }
+
+  f32x16 dqacc[MB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i) dqacc[i] = f32x16{};
+
+  const __bf16* kbase = a.k + (int64_t)kvh * a.k_hs;
+  const __bf16* vbase = a.v + (int64_t)kvh * a.v_hs;
+  u32x4 kreg[PERT], vreg[PERT];
+  auto tile_of = [&](int t) { return t < nP ? pidx[t] : fidx[t - nP]; };
+  auto gload = [&](int n) {
+#pragma unroll
+    for (int i = 0; i < PERT; ++i) {
+      const int idx = tid + NT * i, r = idx / NCH, c = idx % NCH;
+      const int key = n * BN_F + r;
+      if (key < a.Tk) {
+        kreg[i] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)key * a.k_ts + 8 * c);
+        vreg[i] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)key * a.v_ts + 8 * c);
+      } else {
+        kreg[i] = u32x4{0, 0, 0, 0};
+        vreg[i] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto lstore = [&](int stage) {
+    char* kt = smem + stage * 2 * TILE_B;
+    char* vt = kt + TILE_B;
+#pragma unroll
+    for (int i = 0; i < PERT; ++i) {
+      const int idx = tid + NT * i, r = idx / NCH, c = idx % NCH;
+      *reinterpret_cast<u32x4*>(kt + lds_off<D>(r, c)) = kreg[i];
+      *reinterpret_cast<u32x4*>(vt + lds_off<D>(r, c)) = vreg[i];
+    }
+  };
+
+  if (nT > 0) {
+    gload(tile_of(0));
+    lstore(0);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < nT; ++t) {
+    const int stage = t & 1;
+    const bool masked = t < nP;
+    const int n = tile_of(t);
+    if (t + 1 < nT) gload(tile_of(t + 1));
+    const char* kt = smem + stage * 2 * TILE_B;
+    const char* vt = kt + TILE_B;
+
+    f32x16 sacc[KB], pacc[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      sacc[kb] = f32x16{};
+      pacc[kb] = f32x16{};
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        const bf16x8 ka = read_row_operand<D>(kt, 32 * kb + l32, 2 * k + h32);
+        sacc[kb] = mfma32(ka, qop[k], sacc[kb]);
+        const bf16x8 va = read_row_operand<D>(vt, 32 * kb + l32, 2 * k + h32);
+        pacc[kb] = mfma32(va, gop[k], pacc[kb]);
+      }
+    }
+
+    uint64_t mk = ~0ull;
+    if (masked) {
+      const int n0 = n * BN_F;
+      mk = 0;
+      for (int si = 0; si < nS; ++si) {
+        const Slice s = load_slice(mv.slices, sidx[si]);
+        int lo, hi;
+        row_interval(s, qrow, lo, hi);
+        lo = max(lo, n0);
+        hi = min(hi, n0 + BN_F - 1);
+        if (lo <= hi) mk |= bit_range(lo - n0, hi - n0);
+      }
+      mk >>= 4 * h32;
+    }
+
+    float ds[KB][16];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const uint32_t w = static_cast<uint32_t>(mk >> (32 * kb));
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pv = __builtin_amdgcn_exp2f(sacc[kb][r] * a.scale_log2 - lse_l2);
+        if (masked && !((w >> (8 * (r >> 2) + (r & 3))) & 1u)) pv = 0.f;
+        ds[kb][r] = pv * (pacc[kb][r] - dval);
+      }
+    }
+
+#pragma unroll
+    for (int c = 0; c < BN_F / 16; ++c) {
+      const int kb = c >> 1, c2 = c & 1;
+      const bf16x8 sb = pack_bf16x8(&ds[kb][8 * c2]);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const bf16x8 ka = read_tr_operand<D>(kt, 32 * kb + 16 * c2 + 4 * h32,
+                                             32 * mb + 16 * (g16 & 1), t16);
+        dqacc[mb] = mfma32(ka, sb, dqacc[mb]);
+      }
+    }
+
+    if (t + 1 < nT) lstore(stage ^ 1);
+    __syncthreads();
+  }
+
+  if (qok) {
+    __bf16* qp = a.dq + (int64_t)qrow * a.dq_ts + (int64_t)head * a.dq_hs;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf16x4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = static_cast<__bf16>(dqacc[mb][4 * j + i] * a.scale);
+        *reinterpret_cast<bf16x4*>(qp + 32 * mb + 8 * j + 4 * h32) = w;
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdArgs& a, int head_dim, int nq_f, int nk_b, hipStream_t stream) {
+  const int64_t rows = (int64_t)a.Tq * a.Hq;
+  if (rows > 0) {
+    const int G = head_dim / 8;
+    const int64_t blocks = (rows * G + NT - 1) / NT;
+    if (head_dim == 128) ffa_bwd_pre_kernel<128><<<dim3((unsigned)blocks), NT, 0, stream>>>(a);
+    else ffa_bwd_pre_kernel<64><<<dim3((unsigned)blocks), NT, 0, stream>>>(a);
+  }
+  const int64_t gk = (int64_t)nk_b * a.Hkv;
+  if (gk > 0) {
+    if (head_dim == 128) {
+      const size_t lds = 2 * (2 * BM_B * 128 * 2 + 2 * BM_B * 4);
+      ffa_bwd_dkdv_kernel<128><<<dim3((unsigned)gk), NT, lds, stream>>>(a);
+    } else {
+      const size_t lds = 2 * (2 * BM_B * 64 * 2 + 2 * BM_B * 4);
+      ffa_bwd_dkdv_kernel<64><<<dim3((unsigned)gk), NT, lds, stream>>>(a);
+    }
+  }
+  const int64_t gq = (int64_t)nq_f * a.Hq;
+  if (gq > 0) {
+    if (head_dim == 128) {
+      const size_t lds = 2 * 2 * BN_F * 128 * 2;
+      ffa_bwd_dq_kernel<128><<<dim3((unsigned)gq), NT, lds, stream>>>(a);
+    } else {
+      const size_t lds = 2 * 2 * BN_F * 64 * 2;
+      ffa_bwd_dq_kernel<64><<<dim3((unsigned)gq), NT, lds, stream>>>(a);
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ffa

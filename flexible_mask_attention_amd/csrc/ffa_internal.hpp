@@ -1,0 +1,307 @@
+// ffa_internal.hpp - shared definitions of the HIP sources of libffa (gfx950).
+//
+// Holds the block-metadata layout, tile shapes, the slice interval helpers and
+// the small wave-level building blocks (MFMA 32x32x16 bf16, LDS swizzle,
+// transposed LDS reads) used by the forward and backward kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/ffa.h"
+
+namespace ffa {
+
+// ---------------------------------------------------------------------------
+// Tile shapes.  The forward and the dQ kernel walk key tiles of BN_F keys for
+// query blocks of BM_F rows (q2k lists); the dK/dV kernel walks query tiles of
+// BM_B rows for key blocks of BN_B keys (k2q lists).  Per-query-block slice
+// lists are built at BM_F granularity; BM_B must divide BM_F.
+// ---------------------------------------------------------------------------
+constexpr int BM_F = 128;
+constexpr int BN_F = 64;
+constexpr int BM_B = 64;
+constexpr int BN_B = 128;
+static_assert(BM_F % BM_B == 0, "bwd query blocks must nest in fwd query blocks");
+
+constexpr uint32_t META_MAGIC = 0x4D414646u;  // "FFAM"
+constexpr int META_VERSION = 1;
+
+// Header at offset 0 of the metadata buffer.  Fields marked (dev) are written
+// by the build kernels; the rest are written from host-known values by the
+// first build kernel.
+struct MetaHeader {
+  uint32_t magic;
+  int32_t version;
+  int32_t status;        // (dev) FFA_META_ERR_* flags
+  int32_t num_slices;
+  int32_t seqlen_q, seqlen_k, head_dim, pad0;
+  int32_t bm_f, bn_f, bm_b, bn_b;
+  int32_t nq_f, nk_f, nq_b, nk_b;   // block counts at both tilings
+  int64_t capacity;      // int32 entries in the variable region
+  int64_t area;          // (dev) exact valid-pair count
+  int64_t nnz[5];        // (dev) q2k full, q2k mask, k2q full, k2q mask, q-block slices
+  int64_t list_off[5];   // (dev) entry offsets of those lists in the variable region
+  int64_t byte_off[9];   // offsets of the fixed arrays (see MetaLayout)
+  int64_t pad1[3];
+};
+static_assert(sizeof(MetaHeader) <= 256, "header must fit in 256 bytes");
+constexpr int64_t HEADER_BYTES = 256;
+
+enum ListId { L_QF = 0, L_QM = 1, L_KF = 2, L_KM = 3, L_QS = 4 };
+
+// Fixed arrays, in this order after the header (int32, each padded to 256 B):
+//   slices[5*S], q2k_full_off[nq_f+1], q2k_mask_off[nq_f+1],
+//   k2q_full_off[nk_b+1], k2q_mask_off[nk_b+1], qs_off[nq_f+1],
+//   sched_f[nq_f], sched_b[nk_b], then the variable region.
+enum FixedId { A_SLICES = 0, A_QF_OFF, A_QM_OFF, A_KF_OFF, A_KM_OFF, A_QS_OFF, A_SCHED_F,
+               A_SCHED_B, A_VAR };
+
+struct MetaLayout {
+  int32_t nq_f, nk_f, nq_b, nk_b;
+  int64_t byte_off[9];
+  int64_t fixed_bytes;
+};
+
+__host__ __device__ inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+__host__ __device__ inline int32_t cdiv(int32_t a, int32_t b) { return (a + b - 1) / b; }
+
+inline MetaLayout meta_layout(int32_t S, int32_t Tq, int32_t Tk) {
+  MetaLayout L;
+  L.nq_f = cdiv(Tq, BM_F);
+  L.nk_f = cdiv(Tk, BN_F);
+  L.nq_b = cdiv(Tq, BM_B);
+  L.nk_b = cdiv(Tk, BN_B);
+  const int64_t counts[8] = {5LL * S, L.nq_f + 1LL, L.nq_f + 1LL, L.nk_b + 1LL, L.nk_b + 1LL,
+                             L.nq_f + 1LL, (int64_t)L.nq_f, (int64_t)L.nk_b};
+  int64_t off = HEADER_BYTES;
+  for (int i = 0; i < 8; ++i) {
+    L.byte_off[i] = off;
+    off += align256(4 * counts[i]);
+  }
+  L.byte_off[A_VAR] = off;
+  L.fixed_bytes = off;
+  return L;
+}
+
+// Device view of a built metadata buffer.
+struct MetaView {
+  const MetaHeader* hdr;
+  const int32_t* slices;
+  const int32_t* qf_off;
+  const int32_t* qm_off;
+  const int32_t* kf_off;
+  const int32_t* km_off;
+  const int32_t* qs_off;
+  const int32_t* sched_f;
+  const int32_t* sched_b;
+  const int32_t* var;
+};
+
+__device__ inline MetaView meta_view(const void* meta) {
+  MetaView v;
+  const char* b = reinterpret_cast<const char*>(meta);
+  v.hdr = reinterpret_cast<const MetaHeader*>(b);
+  v.slices = reinterpret_cast<const int32_t*>(b + v.hdr->byte_off[A_SLICES]);
+  v.qf_off = reinterpret_cast<const int32_t*>(b + v.hdr->byte_off[A_QF_OFF]);
+  v.qm_off = reinterpret_cast<const int32_t*>(b + v.hdr->byte_off[A_QM_OFF]);
+  v.kf_off = reinterpret_cast<const int32_t*>(b + v.hdr->byte_off[A_KF_OFF]);
+  v.km_off = reinterpret_cast<const int32_t*>(b + v.hdr->byte_off[A_KM_OFF]);
+  v.qs_off = reinterpret_cast<const int32_t*>(b + v.hdr->byte_off[A_QS_OFF]);
+  v.sched_f = reinterpret_cast<const int32_t*>(b + v.hdr->byte_off[A_SCHED_F]);
+  v.sched_b = reinterpret_cast<const int32_t*>(b + v.hdr->byte_off[A_SCHED_B]);
+  v.var = reinterpret_cast<const int32_t*>(b + v.hdr->byte_off[A_VAR]);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Slice intervals.  For slice (q0,q1,k0,k1,t) the valid keys of query row i
+// form one interval, and so do the valid queries of key column j; both are
+// the mask predicate solved for one coordinate.  Inclusive bounds; lo > hi
+// means empty.
+// ---------------------------------------------------------------------------
+struct Slice {
+  int32_t q0, q1, k0, k1, t;
+};
+
+__device__ __forceinline__ Slice load_slice(const int32_t* s, int idx) {
+  Slice r;
+  r.q0 = s[5 * idx + 0];
+  r.q1 = s[5 * idx + 1];
+  r.k0 = s[5 * idx + 2];
+  r.k1 = s[5 * idx + 3];
+  r.t = s[5 * idx + 4];
+  return r;
+}
+
+__device__ __forceinline__ bool slice_ok(const Slice& s, int Tq, int Tk) {
+  return 0 <= s.q0 && s.q0 <= s.q1 && s.q1 <= Tq && 0 <= s.k0 && s.k0 <= s.k1 && s.k1 <= Tk &&
+         s.t >= 0 && s.t <= 3;
+}
+
+// keys valid for query row i: c in [lo_c, hi_c] with c = j - k0
+__device__ __forceinline__ void row_interval(const Slice& s, int i, int& lo, int& hi) {
+  const int r = i - s.q0, Lq = s.q1 - s.q0, Lk = s.k1 - s.k0;
+  const bool inv = (s.t == FFA_INV_CAUSAL) | (s.t == FFA_BI_CAUSAL);
+  const bool cau = (s.t == FFA_CAUSAL) | (s.t == FFA_BI_CAUSAL);
+  int l = inv ? r : 0;
+  int h = cau ? min(Lk - 1, r + Lk - Lq) : Lk - 1;
+  if (i < s.q0 || i >= s.q1) { l = 1; h = 0; }
+  lo = s.k0 + l;
+  hi = s.k0 + h;
+}
+
+// queries valid for key column j: r in [lo_r, hi_r] with r = i - q0
+__device__ __forceinline__ void col_interval(const Slice& s, int j, int& lo, int& hi) {
+  const int c = j - s.k0, Lq = s.q1 - s.q0, Lk = s.k1 - s.k0;
+  const bool inv = (s.t == FFA_INV_CAUSAL) | (s.t == FFA_BI_CAUSAL);
+  const bool cau = (s.t == FFA_CAUSAL) | (s.t == FFA_BI_CAUSAL);
+  int l = cau ? max(0, c - (Lk - Lq)) : 0;
+  int h = inv ? min(Lq - 1, c) : Lq - 1;
+  if (j < s.k0 || j >= s.k1) { l = 1; h = 0; }
+  lo = s.q0 + l;
+  hi = s.q0 + h;
+}
+
+// bits [a, b] of a 64-bit word (0 <= a <= b <= 63)
+__device__ __forceinline__ uint64_t bit_range(int a, int b) {
+  return (~0ull >> (63 - (b - a))) << a;
+}
+
+// ---------------------------------------------------------------------------
+// MFMA and register types.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+// D = A(32x16) * B(16x32) + C, fp32 accumulate.  Lane l holds A[l%32][8*(l/32)+e],
+// B[8*(l/32)+e][l%32] (e = 0..7) and C[8*(r/4) + 4*(l/32) + r%4][l%32] in register r.
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 pack_bf16x8(const float* x) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = static_cast<__bf16>(x[e]);
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// LDS tiles of [rows][D] bf16 stored in 16-byte chunks.  Chunk c of row r sits
+// at chunk position c ^ swz(r).  swz keeps both access patterns conflict-free:
+// 16 consecutive rows reading one chunk (128-bit operand reads) and 4
+// consecutive rows x 4 adjacent chunks (transposed 64-bit reads).
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) {
+    return ((r & 3) << 2) | ((r >> 2) & 3);
+  } else {
+    return (((r & 3) << 1) | ((r >> 2) & 1)) & 7;
+  }
+}
+
+template <int D>
+__device__ __forceinline__ int lds_off(int r, int c) {  // byte offset of chunk c of row r
+  return r * (D * 2) + ((c ^ swz<D>(r)) << 4);
+}
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+
+// Transposed read: within each 16-lane group, lane t returns column t of the
+// 4 x 16 block of bf16 whose row e is the 32 bytes loaded by lanes 4e..4e+3.
+// Each lane passes the LDS byte address of its own 8-byte piece.
+__device__ __forceinline__ i16x4 ds_read_tr16(const char* lds_base, int byte_off) {
+  const __attribute__((address_space(3))) char* p =
+      (const __attribute__((address_space(3))) char*)(lds_base) + byte_off;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p);
+}
+
+// 8 bf16 of an MFMA operand whose rows are {r0..r0+3} and {r0+8..r0+11} of a
+// swizzled [rows][D] tile, column `col` (= this lane's output index).
+// lane t of each 16-lane group reads row r0 + t/4 (+8), columns
+// colbase + 4*(t%4) .. +3, where colbase = col - t.
+template <int D>
+__device__ __forceinline__ bf16x8 read_tr_operand(const char* tile, int r0, int colbase, int t) {
+  const int rr = r0 + (t >> 2);
+  const int cc = colbase + 4 * (t & 3);           // first column of this lane's 8-byte piece
+  const int o1 = lds_off<D>(rr, cc >> 3) + ((cc & 7) << 1);
+  const int o2 = lds_off<D>(rr + 8, cc >> 3) + ((cc & 7) << 1);
+  i16x4 a = ds_read_tr16(tile, o1);
+  i16x4 b = ds_read_tr16(tile, o2);
+  bf16x8 r;
+  __builtin_memcpy(&r, &a, 8);
+  __builtin_memcpy(reinterpret_cast<char*>(&r) + 8, &b, 8);
+  return r;
+}
+
+// 128-bit operand read: row r, chunk c of a swizzled tile.
+template <int D>
+__device__ __forceinline__ bf16x8 read_row_operand(const char* tile, int r, int c) {
+  const __attribute__((address_space(3))) char* p =
+      (const __attribute__((address_space(3))) char*)(tile) + lds_off<D>(r, c);
+  bf16x8 v;
+  u32x4 u = *(const __attribute__((address_space(3))) u32x4*)p;
+  __builtin_memcpy(&v, &u, 16);
+  return v;
+}
+
+__device__ __forceinline__ float wave_swap_max(float x) {
+  auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+
+__device__ __forceinline__ float wave_swap_sum(float x) {
+  auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+// Host-side launchers (one per source file).
+hipError_t launch_build_meta(const int32_t* d_slices, int32_t S, int32_t Tq, int32_t Tk,
+                             int32_t head_dim, void* d_meta, int64_t capacity,
+                             const MetaLayout& L, hipStream_t stream);
+
+struct FwdArgs {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  __bf16* o;
+  float* lse;
+  const void* meta;
+  int64_t q_ts, q_hs, k_ts, k_hs, v_ts, v_hs, o_ts, o_hs;
+  int32_t Tq, Tk, Hq, Hkv;
+  float scale_log2;   // softmax_scale * log2(e)
+  float scale;
+};
+hipError_t launch_fwd(const FwdArgs& a, int head_dim, int nq_f, hipStream_t stream);
+
+struct BwdArgs {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  const __bf16* o;
+  const __bf16* dout;
+  const float* lse;
+  float* dvec;        // workspace: D_i = dO_i . O_i, [Hq][Tq]
+  __bf16* dq;
+  __bf16* dk;
+  __bf16* dv;
+  const void* meta;
+  int64_t q_ts, q_hs, k_ts, k_hs, v_ts, v_hs, o_ts, o_hs, do_ts, do_hs;
+  int64_t dq_ts, dq_hs, dk_ts, dk_hs, dv_ts, dv_hs;
+  int32_t Tq, Tk, Hq, Hkv;
+  float scale_log2;
+  float scale;
+};
+hipError_t launch_bwd(const BwdArgs& a, int head_dim, int nq_f, int nk_b, hipStream_t stream);
+
+}  // namespace ffa

@@ -1,0 +1,467 @@
+// ffa_meta.hip - block metadata of a slice table on gfx950.
+//
+// For every tile (query block x key block) the exact number v of valid
+// (query, key) pairs is counted and the tile is classed Empty (v = 0), Full
+// (no masking needed) or Partial (masking needed); the non-empty tiles of each
+// block are listed in CSR form, Full and Partial apart.  This follows the
+// create_block_mask kernel and CSR compression of the MagiAttention
+// documentation page, "FFA_FA4" optimisations, items 1 and 2 (q2k for the
+// forward, k2q for the backward, out-of-bounds-in-q-only blocks count as Full
+// in the forward), rebuilt for AttnSlice tables:
+//
+//   q2k: owner = query block of BM_F rows, iterated = key blocks of BN_F.
+//        Rows past seqlen_q are ignored; keys past seqlen_k are invalid.
+//        Full iff v == rows_in_bounds * BN_F.
+//   k2q: owner = key block of BN_B keys, iterated = query blocks of BM_B.
+//        Keys past seqlen_k are ignored; rows past seqlen_q are invalid.
+//        Full iff v == keys_in_bounds * BM_B.
+//
+// Counting: each owner position (a row for q2k, a key for k2q) has one valid
+// interval per slice along the iterated axis.  An interval adds its length
+// clipped to the two end blocks directly, and whole blocks in between through
+// a difference array; a prefix sum then gives v for every iterated block.
+// All integer work, so the result is exact and order independent.
+#include "ffa_internal.hpp"
+
+namespace ffa {
+
+namespace {
+
+constexpr int MT = 256;     // threads of the tile kernels
+constexpr int CH = 4096;    // iterated blocks per LDS chunk
+constexpr int PER = CH / MT;
+
+struct MetaPtrs {
+  MetaHeader* hdr;
+  int32_t* slices;
+  int32_t* qf_off;
+  int32_t* qm_off;
+  int32_t* kf_off;
+  int32_t* km_off;
+  int32_t* qs_off;
+  int32_t* sched_f;
+  int32_t* sched_b;
+  int32_t* var;
+};
+
+__device__ MetaPtrs meta_ptrs(void* meta) {
+  char* b = reinterpret_cast<char*>(meta);
+  MetaPtrs p;
+  p.hdr = reinterpret_cast<MetaHeader*>(b);
+  p.slices = reinterpret_cast<int32_t*>(b + p.hdr->byte_off[A_SLICES]);
+  p.qf_off = reinterpret_cast<int32_t*>(b + p.hdr->byte_off[A_QF_OFF]);
+  p.qm_off = reinterpret_cast<int32_t*>(b + p.hdr->byte_off[A_QM_OFF]);
+  p.kf_off = reinterpret_cast<int32_t*>(b + p.hdr->byte_off[A_KF_OFF]);
+  p.km_off = reinterpret_cast<int32_t*>(b + p.hdr->byte_off[A_KM_OFF]);
+  p.qs_off = reinterpret_cast<int32_t*>(b + p.hdr->byte_off[A_QS_OFF]);
+  p.sched_f = reinterpret_cast<int32_t*>(b + p.hdr->byte_off[A_SCHED_F]);
+  p.sched_b = reinterpret_cast<int32_t*>(b + p.hdr->byte_off[A_SCHED_B]);
+  p.var = reinterpret_cast<int32_t*>(b + p.hdr->byte_off[A_VAR]);
+  return p;
+}
+
+struct InitArgs {
+  int32_t S, Tq, Tk, head_dim;
+  int32_t nq_f, nk_f, nq_b, nk_b;
+  int64_t capacity;
+  int64_t byte_off[9];
+};
+
+// Header fields, counters, and a copy of the slice table.
+__global__ void meta_init_kernel(const int32_t* __restrict__ slices, void* meta, InitArgs a) {
+  char* b = reinterpret_cast<char*>(meta);
+  MetaHeader* h = reinterpret_cast<MetaHeader*>(b);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    h->magic = META_MAGIC;
+    h->version = META_VERSION;
+    h->status = 0;
+    h->num_slices = a.S;
+    h->seqlen_q = a.Tq;
+    h->seqlen_k = a.Tk;
+    h->head_dim = a.head_dim;
+    h->pad0 = 0;
+    h->bm_f = BM_F;
+    h->bn_f = BN_F;
+    h->bm_b = BM_B;
+    h->bn_b = BN_B;
+    h->nq_f = a.nq_f;
+    h->nk_f = a.nk_f;
+    h->nq_b = a.nq_b;
+    h->nk_b = a.nk_b;
+    h->capacity = a.capacity;
+    h->area = 0;
+    for (int i = 0; i < 5; ++i) {
+      h->nnz[i] = 0;
+      h->list_off[i] = 0;
+    }
+    for (int i = 0; i < 9; ++i) h->byte_off[i] = a.byte_off[i];
+  }
+  int32_t* dst = reinterpret_cast<int32_t*>(b + a.byte_off[A_SLICES]);
+  const int n = 5 * a.S;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+    dst[i] = slices[i];
+}
+
+// Per-slice bounds / type checks and pairwise disjointness, one thread per
+// ordered pair (a <= b).  Two slices overlap iff some shared row has
+// intersecting key intervals.
+__global__ void meta_validate_kernel(void* meta) {
+  MetaPtrs p = meta_ptrs(meta);
+  const int S = p.hdr->num_slices, Tq = p.hdr->seqlen_q, Tk = p.hdr->seqlen_k;
+  const int a = blockIdx.y * 16 + threadIdx.y;
+  const int b = blockIdx.x * 16 + threadIdx.x;
+  if (a >= S || b >= S || b < a) return;
+  const Slice sa = load_slice(p.slices, a);
+  if (a == b) {
+    const bool bounds = 0 <= sa.q0 && sa.q0 <= sa.q1 && sa.q1 <= Tq && 0 <= sa.k0 &&
+                        sa.k0 <= sa.k1 && sa.k1 <= Tk;
+    int flags = 0;
+    if (!bounds) flags |= FFA_META_ERR_BOUNDS;
+    else if (sa.t < 0 || sa.t > 3) flags |= FFA_META_ERR_TYPE;
+    if (flags) atomicOr(&p.hdr->status, flags);
+    return;
+  }
+  const Slice sb = load_slice(p.slices, b);
+  if (!slice_ok(sa, Tq, Tk) || !slice_ok(sb, Tq, Tk)) return;
+  const int r0 = max(sa.q0, sb.q0), r1 = min(sa.q1, sb.q1);
+  if (r0 >= r1 || max(sa.k0, sb.k0) >= min(sa.k1, sb.k1)) return;
+  for (int i = r0; i < r1; ++i) {
+    int la, ha, lb, hb;
+    row_interval(sa, i, la, ha);
+    row_interval(sb, i, lb, hb);
+    if (la <= ha && lb <= hb && max(la, lb) <= min(ha, hb)) {
+      atomicOr(&p.hdr->status, FFA_META_ERR_OVERLAP);
+      return;
+    }
+  }
+}
+
+// Block-wide exclusive scan of one int per thread (MT threads); returns the
+// exclusive prefix and writes the block total to *total.
+__device__ int block_exclusive_scan(int x, int* lds_ws, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int incl = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) lds_ws[w] = incl;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < MT / 64; ++i) {
+    int v = lds_ws[i];
+    if (i < w) base += v;
+    tot += v;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + incl - x;
+}
+
+// One owner block of the q2k (DIR = 0) or k2q (DIR = 1) classification.
+// FILL = false: write the Full / Partial counts of the owner (and, for q2k,
+// its slice count and area).  FILL = true: write the ascending index lists.
+template <int DIR, bool FILL>
+__global__ __launch_bounds__(MT) void meta_tiles_kernel(void* meta) {
+  __shared__ int cnt[CH];
+  __shared__ int diff[CH + 1];
+  __shared__ int slist[MT];
+  __shared__ int ws[MT / 64 + 1];
+  __shared__ int sh_minmax[2];
+
+  MetaPtrs p = meta_ptrs(meta);
+  const MetaHeader* h = p.hdr;
+  const int S = h->num_slices, Tq = h->seqlen_q, Tk = h->seqlen_k;
+  const int own = blockIdx.x;
+  // owner axis A and iterated axis B
+  const int BA = DIR == 0 ? BM_F : BN_B;
+  const int BB = DIR == 0 ? BN_F : BM_B;
+  const int TA = DIR == 0 ? Tq : Tk;
+  const int a0 = own * BA, a1 = min(a0 + BA, TA);
+  const int cap = (a1 - a0) * BB;     // valid count of a Full tile
+  const int tid = threadIdx.x;
+
+  int32_t* full_off = DIR == 0 ? p.qf_off : p.kf_off;
+  int32_t* mask_off = DIR == 0 ? p.qm_off : p.km_off;
+  const int64_t capacity = h->capacity;
+  int out_f = 0, out_p = 0;   // running positions (FILL)
+  int64_t base_f = 0, base_p = 0;
+  if (FILL) {
+    base_f = h->list_off[DIR == 0 ? L_QF : L_KF] + full_off[own];
+    base_p = h->list_off[DIR == 0 ? L_QM : L_KM] + mask_off[own];
+  }
+
+  // pass 1: iterated-block range touched by slices meeting this owner block,
+  // and (q2k) the owner's slice list
+  if (tid == 0) {
+    sh_minmax[0] = 0x7fffffff;
+    sh_minmax[1] = -1;
+  }
+  __syncthreads();
+  int nslices_here = 0;
+  int64_t qs_base = 0;
+  if (FILL && DIR == 0) qs_base = h->list_off[L_QS] + p.qs_off[own];
+  for (int sb = 0; sb < S; sb += MT) {
+    const int si = sb + tid;
+    int hit = 0;
+    if (si < S) {
+      const Slice s = load_slice(p.slices, si);
+      if (slice_ok(s, Tq, Tk) && s.q1 > s.q0 && s.k1 > s.k0) {
+        const int sa0 = DIR == 0 ? s.q0 : s.k0, sa1 = DIR == 0 ? s.q1 : s.k1;
+        const int sb0 = DIR == 0 ? s.k0 : s.q0, sb1 = DIR == 0 ? s.k1 : s.q1;
+        if (sa0 < a1 && sa1 > a0) {
+          hit = 1;
+          atomicMin(&sh_minmax[0], sb0 / BB);
+          atomicMax(&sh_minmax[1], (sb1 - 1) / BB);
+        }
+      }
+    }
+    if (DIR == 0) {
+      int tot;
+      const int pos = block_exclusive_scan(hit, ws, &tot);
+      if (FILL && hit) {
+        const int64_t at = qs_base + nslices_here + pos;
+        if (at < capacity) p.var[at] = si;
+      }
+      nslices_here += tot;
+    }
+  }
+  __syncthreads();
+  const int bmin = sh_minmax[0], bmax = sh_minmax[1];
+  if (!FILL && DIR == 0 && tid == 0) p.qs_off[own + 1] = nslices_here;
+
+  int64_t area = 0;
+  for (int cb0 = bmin; cb0 <= bmax; cb0 += CH) {
+    const int cb1 = min(cb0 + CH, bmax + 1);   // blocks [cb0, cb1)
+    for (int i = tid; i < CH + 1; i += MT) {
+      if (i < CH) cnt[i] = 0;
+      diff[i] = 0;
+    }
+    __syncthreads();
+    const int lo_lim = cb0 * BB, hi_lim = cb1 * BB - 1;
+    for (int sb = 0; sb < S; sb += MT) {
+      // compact the slices of this group that meet the owner block
+      const int si = sb + tid;
+      int hit = 0;
+      if (si < S) {
+        const Slice s = load_slice(p.slices, si);
+        if (slice_ok(s, Tq, Tk) && s.q1 > s.q0 && s.k1 > s.k0) {
+          const int sa0 = DIR == 0 ? s.q0 : s.k0, sa1 = DIR == 0 ? s.q1 : s.k1;
+          const int sb0 = DIR == 0 ? s.k0 : s.q0, sb1 = DIR == 0 ? s.k1 : s.q1;
+          hit = (sa0 < a1 && sa1 > a0 && sb0 <= hi_lim && sb1 > lo_lim) ? 1 : 0;
+        }
+      }
+      int tot;
+      const int pos = block_exclusive_scan(hit, ws, &tot);
+      if (hit) slist[pos] = si;
+      __syncthreads();
+      // every (slice, owner position) pair adds its interval
+      for (int w = tid; w < tot * BA; w += MT) {
+        const int pa = a0 + (w % BA);
+        if (pa >= a1) continue;
+        const Slice s = load_slice(p.slices, slist[w / BA]);
+        int lo, hi;
+        if (DIR == 0) row_interval(s, pa, lo, hi);
+        else col_interval(s, pa, lo, hi);
+        lo = max(lo, lo_lim);
+        hi = min(hi, hi_lim);
+        if (lo > hi) continue;
+        const int bl = lo / BB - cb0, bh = hi / BB - cb0;
+        if (bl == bh) {
+          atomicAdd(&cnt[bl], hi - lo + 1);
+        } else {
+          atomicAdd(&cnt[bl], (bl + cb0 + 1) * BB - lo);
+          atomicAdd(&cnt[bh], hi - (bh + cb0) * BB + 1);
+          if (bh > bl + 1) {
+            atomicAdd(&diff[bl + 1], BB);
+            atomicAdd(&diff[bh], -BB);
+          }
+        }
+      }
+      __syncthreads();
+    }
+    // prefix sum of diff over the chunk: thread tid owns PER consecutive blocks
+    int run = 0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) run += diff[tid * PER + e];
+    int dummy;
+    int carry = block_exclusive_scan(run, ws, &dummy);
+    int nf = 0, np = 0;
+    int vals[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      carry += diff[tid * PER + e];
+      const int b = tid * PER + e;
+      const int v = (b < cb1 - cb0) ? cnt[b] + carry : 0;
+      vals[e] = v;
+      area += v;
+      nf += (v != 0 && v == cap);
+      np += (v != 0 && v != cap);
+    }
+    int tf, tp;
+    const int pf = block_exclusive_scan(nf, ws, &tf);
+    const int pp = block_exclusive_scan(np, ws, &tp);
+    if (FILL) {
+      int of = out_f + pf, op = out_p + pp;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        const int v = vals[e];
+        const int bidx = cb0 + tid * PER + e;
+        if (v != 0 && v == cap) {
+          const int64_t at = base_f + of++;
+          if (at < capacity) p.var[at] = bidx;
+        } else if (v != 0) {
+          const int64_t at = base_p + op++;
+          if (at < capacity) p.var[at] = bidx;
+        }
+      }
+    }
+    out_f += tf;
+    out_p += tp;
+    __syncthreads();
+  }
+  if (!FILL) {
+    if (tid == 0) {
+      full_off[own + 1] = out_f;
+      mask_off[own + 1] = out_p;
+    }
+    if (DIR == 0) {
+      // block-reduce the area (int64) and add once per owner
+      __shared__ long long sarea[MT / 64];
+      long long x = area;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+      if ((tid & 63) == 0) sarea[tid >> 6] = x;
+      __syncthreads();
+      if (tid == 0) {
+        long long t = 0;
+        for (int i = 0; i < MT / 64; ++i) t += sarea[i];
+        if (t) atomicAdd(reinterpret_cast<unsigned long long*>(&p.hdr->area),
+                         static_cast<unsigned long long>(t));
+      }
+    }
+  }
+}
+
+// Turn the per-owner counts stored at [1..n] into offsets (in place) and lay
+// out the variable region.  One block of 1024 threads.
+__device__ void scan_inplace(int32_t* a, int n, int* ws) {
+  // a[0] = 0; inclusive scan of a[1..n]
+  const int tid = threadIdx.x, NT = blockDim.x;
+  const int lane = tid & 63, w = tid >> 6;
+  if (tid == 0) a[0] = 0;
+  int carry = 0;
+  for (int base = 1; base <= n; base += NT) {
+    const int i = base + tid;
+    int x = (i <= n) ? a[i] : 0;
+    int incl = x;
+    for (int o = 1; o < 64; o <<= 1) {
+      int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63) ws[w] = incl;
+    __syncthreads();
+    int pre = 0, tot = 0;
+    for (int j = 0; j < NT / 64; ++j) {
+      if (j < w) pre += ws[j];
+      tot += ws[j];
+    }
+    if (i <= n) a[i] = carry + pre + incl;
+    carry += tot;
+    __syncthreads();
+  }
+}
+
+__global__ void meta_scan_kernel(void* meta) {
+  __shared__ int ws[16];
+  MetaPtrs p = meta_ptrs(meta);
+  MetaHeader* h = p.hdr;
+  scan_inplace(p.qf_off, h->nq_f, ws);
+  scan_inplace(p.qm_off, h->nq_f, ws);
+  scan_inplace(p.kf_off, h->nk_b, ws);
+  scan_inplace(p.km_off, h->nk_b, ws);
+  scan_inplace(p.qs_off, h->nq_f, ws);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int64_t n0 = p.qf_off[h->nq_f], n1 = p.qm_off[h->nq_f];
+    const int64_t n2 = p.kf_off[h->nk_b], n3 = p.km_off[h->nk_b];
+    const int64_t n4 = p.qs_off[h->nq_f];
+    h->nnz[0] = n0;
+    h->nnz[1] = n1;
+    h->nnz[2] = n2;
+    h->nnz[3] = n3;
+    h->nnz[4] = n4;
+    h->list_off[0] = 0;
+    h->list_off[1] = n0;
+    h->list_off[2] = n0 + n1;
+    h->list_off[3] = n0 + n1 + n2;
+    h->list_off[4] = n0 + n1 + n2 + n3;
+    if (n0 + n1 + n2 + n3 + n4 > h->capacity) atomicOr(&h->status, FFA_META_ERR_CAPACITY);
+  }
+}
+
+// Longest-first order of owners: rank = number of owners with more work, ties
+// broken by index.  Work = 4 per Full tile + 5 per Partial tile.  Owners past
+// MAX_SORT keep their natural order.
+constexpr int MAX_SORT = 32768;
+
+__global__ void meta_schedule_kernel(void* meta) {
+  MetaPtrs p = meta_ptrs(meta);
+  const MetaHeader* h = p.hdr;
+  const int which = blockIdx.y;   // 0: fwd q-blocks, 1: bwd k-blocks
+  const int n = which == 0 ? h->nq_f : h->nk_b;
+  const int32_t* fo = which == 0 ? p.qf_off : p.kf_off;
+  const int32_t* mo = which == 0 ? p.qm_off : p.km_off;
+  int32_t* out = which == 0 ? p.sched_f : p.sched_b;
+  const int o = blockIdx.x * blockDim.x + threadIdx.x;
+  if (o >= n) return;
+  if (n > MAX_SORT) {
+    out[o] = o;
+    return;
+  }
+  auto cost = [&](int x) { return 4 * (fo[x + 1] - fo[x]) + 5 * (mo[x + 1] - mo[x]); };
+  const int c = cost(o);
+  int rank = 0;
+  for (int x = 0; x < n; ++x) {
+    const int cx = cost(x);
+    rank += (cx > c) || (cx == c && x < o);
+  }
+  out[rank] = o;
+}
+
+}  // namespace
+
+hipError_t launch_build_meta(const int32_t* d_slices, int32_t S, int32_t Tq, int32_t Tk,
+                             int32_t head_dim, void* d_meta, int64_t capacity,
+                             const MetaLayout& L, hipStream_t stream) {
+  InitArgs ia;
+  ia.S = S;
+  ia.Tq = Tq;
+  ia.Tk = Tk;
+  ia.head_dim = head_dim;
+  ia.nq_f = L.nq_f;
+  ia.nk_f = L.nk_f;
+  ia.nq_b = L.nq_b;
+  ia.nk_b = L.nk_b;
+  ia.capacity = capacity;
+  for (int i = 0; i < 9; ++i) ia.byte_off[i] = L.byte_off[i];
+  const int n5 = 5 * S;
+  const int gi = n5 > 0 ? min(1024, (n5 + 255) / 256) : 1;
+  meta_init_kernel<<<gi, 256, 0, stream>>>(d_slices, d_meta, ia);
+  if (S > 0) {
+    dim3 g((S + 15) / 16, (S + 15) / 16);
+    meta_validate_kernel<<<g, dim3(16, 16), 0, stream>>>(d_meta);
+  }
+  if (L.nq_f > 0) meta_tiles_kernel<0, false><<<L.nq_f, MT, 0, stream>>>(d_meta);
+  if (L.nk_b > 0) meta_tiles_kernel<1, false><<<L.nk_b, MT, 0, stream>>>(d_meta);
+  meta_scan_kernel<<<1, 1024, 0, stream>>>(d_meta);
+  if (L.nq_f > 0) meta_tiles_kernel<0, true><<<L.nq_f, MT, 0, stream>>>(d_meta);
+  if (L.nk_b > 0) meta_tiles_kernel<1, true><<<L.nk_b, MT, 0, stream>>>(d_meta);
+  const int nmax = max(L.nq_f, L.nk_b);
+  if (nmax > 0) meta_schedule_kernel<<<dim3((nmax + 255) / 256, 2), 256, 0, stream>>>(d_meta);
+  return hipGetLastError();
+}
+
+}  // namespace ffa

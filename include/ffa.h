@@ -1,0 +1,192 @@
+/*
+ * ffa.h - C ABI of libffa: Flex-Flash-Attention (FFA) on AMD Instinct MI355X (gfx950).
+ *
+ * FFA is fused attention forward and backward over a list of AttnSlices.  An
+ * AttnSlice is (QRange, KRange, MaskType): a contiguous 2-D region of the
+ * query x key plane plus the rule that applies inside it (MagiAttention blog
+ * deep-dive, section "Flex-Flash-Attention 与 AttnSlice", AttnSlice equation
+ * and the list of mask types after it).  A list of such slices expresses
+ * varlen, block-causal, sliding-window and patch-and-pack masks in one call.
+ *
+ * Conventions used by every entry point
+ * -------------------------------------
+ *  - Slice table: device int32 array [num_slices][5] =
+ *      { q_start, q_end, k_start, k_end, mask_type }, half-open token ranges
+ *    into the q and k tensors.  For slice s, query i and key j with
+ *    r = i - q_start, c = j - k_start, Lq = q_end - q_start, Lk = k_end - k_start,
+ *    (i, j) is valid iff it lies in the rectangle and
+ *      FFA_FULL:        always
+ *      FFA_CAUSAL:      c <= r + (Lk - Lq)       (bottom-right aligned)
+ *      FFA_INV_CAUSAL:  c >= r                   (top-left aligned)
+ *      FFA_BI_CAUSAL:   both.
+ *    Slices must have disjoint valid sets.  A query attends to the union of its
+ *    valid keys; a query with none gets O = 0 and LSE = -inf.
+ *  - Tensors are token-major ("THD"): q, o, dout, dq are [seqlen_q][num_heads_q][head_dim],
+ *    k, v, dk, dv are [seqlen_k][num_heads_kv][head_dim], all bf16, with the
+ *    last dimension contiguous and arbitrary token/head strides (in elements).
+ *    Query head h reads key/value head h / (num_heads_q / num_heads_kv).
+ *  - lse is fp32 [num_heads_q][seqlen_q], natural log, including the softmax
+ *    scale: lse_i = ln sum_{j valid} exp(scale * q_i . k_j).
+ *  - Ownership: the caller allocates and frees every buffer.  The library
+ *    allocates nothing, keeps no global mutable state, never synchronises, and
+ *    only enqueues work on the given stream (a hipStream_t passed as void*;
+ *    NULL is the default stream).
+ *  - Errors: problems visible on the host (null or misaligned pointers, bad
+ *    shapes or strides, unsupported head_dim, a buffer that is too small) make
+ *    the call return a non-zero ffa_status before anything is enqueued.  A
+ *    failed launch returns FFA_ERR_HIP.  Problems in the device-resident slice
+ *    table are found by ffa_build_block_meta on the device and recorded in the
+ *    metadata's status word (FFA_META_ERR_* flags); ffa_fwd and ffa_bwd then
+ *    write nothing.  No function throws.
+ */
+#ifndef FFA_H_
+#define FFA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FFA_ABI_VERSION 1
+
+#if defined(__GNUC__)
+#define FFA_API __attribute__((visibility("default")))
+#else
+#define FFA_API
+#endif
+
+typedef enum {
+  FFA_FULL = 0,
+  FFA_CAUSAL = 1,
+  FFA_INV_CAUSAL = 2,
+  FFA_BI_CAUSAL = 3
+} ffa_mask_type;
+
+typedef enum {
+  FFA_OK = 0,
+  FFA_ERR_INVALID_ARGUMENT = 1,    /* null/misaligned pointer, bad shape or stride */
+  FFA_ERR_UNSUPPORTED = 2,         /* e.g. head_dim not 64 or 128 */
+  FFA_ERR_WORKSPACE_TOO_SMALL = 3, /* meta_bytes or ws_bytes below the required size */
+  FFA_ERR_HIP = 4                  /* a kernel launch failed */
+} ffa_status;
+
+/* Flags of the device status word inside the block metadata. */
+#define FFA_META_ERR_BOUNDS 1   /* a range outside [0, seqlen] or start > end */
+#define FFA_META_ERR_TYPE 2     /* mask_type not in 0..3 */
+#define FFA_META_ERR_OVERLAP 4  /* two slices share a valid (query, key) pair */
+#define FFA_META_ERR_CAPACITY 8 /* meta buffer too small for this table's CSR lists */
+
+typedef struct {
+  const void* ptr;       /* device, 16-byte aligned */
+  int64_t token_stride;  /* elements between consecutive tokens (multiple of 8) */
+  int64_t head_stride;   /* elements between consecutive heads (multiple of 8) */
+} ffa_tensor_in;
+
+typedef struct {
+  void* ptr;
+  int64_t token_stride;
+  int64_t head_stride;
+} ffa_tensor_out;
+
+typedef struct {
+  int32_t seqlen_q;      /* >= 0 */
+  int32_t seqlen_k;      /* >= 0 */
+  int32_t num_heads_q;   /* >= 1, multiple of num_heads_kv */
+  int32_t num_heads_kv;  /* >= 1 */
+  int32_t head_dim;      /* 64 or 128 */
+  float softmax_scale;   /* finite, non-zero; 1/sqrt(head_dim) is the usual choice */
+} ffa_shape;
+
+/* Host-side summary of a block-metadata buffer (pure pointer arithmetic; no
+ * device access).  Tile shapes are the kernels' own; they are what the CSR
+ * lists are built for. */
+typedef struct {
+  int32_t bm_fwd, bn_fwd;            /* q2k tile: query rows x key cols */
+  int32_t bm_bwd, bn_bwd;            /* k2q tile: query rows x key cols */
+  int32_t num_qblocks_fwd, num_kblocks_fwd;
+  int32_t num_qblocks_bwd, num_kblocks_bwd;
+  int64_t header_bytes;              /* the header struct below sits at offset 0 */
+  /* device pointers into the buffer */
+  const int32_t* status;             /* FFA_META_ERR_* flags, 0 = good */
+  const int64_t* area;               /* exact number of valid (query, key) pairs */
+  const int32_t* full_block_offset;  /* q2k, [num_qblocks_fwd + 1] */
+  const int32_t* mask_block_offset;  /* q2k, [num_qblocks_fwd + 1] */
+  const int32_t* k2q_full_block_offset; /* k2q, [num_kblocks_bwd + 1] */
+  const int32_t* k2q_mask_block_offset; /* k2q, [num_kblocks_bwd + 1] */
+  const int32_t* qblock_slice_offset;   /* [num_qblocks_fwd + 1] */
+  const int32_t* schedule_fwd;       /* [num_qblocks_fwd], q-blocks by descending work */
+  const int32_t* schedule_bwd;       /* [num_kblocks_bwd], k-blocks by descending work */
+  const int32_t* index_base;         /* variable region; see list_offsets */
+  const int64_t* list_offsets;       /* device int64[5]: entry offsets from index_base of
+                                        full_block_idx, mask_block_idx, k2q_full_block_idx,
+                                        k2q_mask_block_idx, qblock_slice_idx */
+} ffa_block_meta_view_t;
+
+/* Upper bound on the metadata buffer size for a table of num_slices slices.
+ * host_slices (nullable) is a host copy of the table: when given, the bound
+ * is tightened from each slice's bounding rectangle, otherwise it assumes
+ * every tile may be non-empty.  Block classes and CSR lists follow the
+ * create_block_mask / CSR description of the MagiAttention documentation
+ * page, "FFA_FA4" optimisations, items 1 and 2. */
+FFA_API ffa_status ffa_block_meta_workspace_size(int32_t num_slices, int32_t seqlen_q,
+                                                 int32_t seqlen_k, int32_t head_dim,
+                                                 const int32_t* host_slices, size_t* bytes);
+
+/* Build the block metadata of a slice table, asynchronously on `stream`.
+ * d_slices: device int32 [num_slices][5] (read only; copied into d_meta).
+ * d_meta: device buffer of meta_bytes bytes, 256-byte aligned, owned by the caller.
+ * For each (query block, key block) tile the valid count v is computed exactly
+ * and the tile is classed Empty (v = 0), Full or Partial.  q2k (forward):
+ * query rows past seqlen_q are ignored and key columns past seqlen_k count as
+ * invalid, so a block out of bounds only in q can be Full.  k2q (backward):
+ * the mirror, key columns past seqlen_k ignored, query rows past seqlen_q
+ * invalid.  Per block the Full and Partial lists are kept apart, ascending
+ * (full_block_offset / mask_block_offset and the k2q mirrors).  The table is
+ * validated on the device (bounds, type, disjointness) into the status word.
+ * The buffer can be reused by any number of ffa_fwd / ffa_bwd calls with the
+ * same seqlens and head_dim until it is rebuilt. */
+FFA_API ffa_status ffa_build_block_meta(const int32_t* d_slices, int32_t num_slices,
+                                        int32_t seqlen_q, int32_t seqlen_k, int32_t head_dim,
+                                        void* d_meta, size_t meta_bytes, void* stream);
+
+/* Fill *out from the layout of a metadata buffer built with these arguments. */
+FFA_API ffa_status ffa_block_meta_view(const void* d_meta, int32_t num_slices, int32_t seqlen_q,
+                                       int32_t seqlen_k, int32_t head_dim,
+                                       ffa_block_meta_view_t* out);
+
+/* Forward: o = softmax(scale * q k^T restricted to the valid set) v and lse,
+ * computed with an online softmax over the q2k Full and Partial tiles of
+ * each query block (per-element masking only on Partial tiles).
+ * o: bf16 like q.  lse: device fp32 [num_heads_q][seqlen_q], 16-byte aligned.
+ * Rows with no valid key get o = 0, lse = -inf. */
+FFA_API ffa_status ffa_fwd(const ffa_shape* shape, ffa_tensor_in q, ffa_tensor_in k,
+                           ffa_tensor_in v, const void* d_meta, ffa_tensor_out o, float* lse,
+                           void* stream);
+
+/* Scratch bytes ffa_bwd needs (the per-row dot products D_i = dO_i . O_i). */
+FFA_API ffa_status ffa_bwd_workspace_size(const ffa_shape* shape, size_t* bytes);
+
+/* Backward: dq, dk, dv of the forward above, given its o and lse.
+ * dk and dv are accumulated per key block in a fixed order over the k2q tiles
+ * and the query heads that share the key head, and dq per query block over
+ * its q2k tiles, so results are bitwise reproducible (no atomics).
+ * d_ws: device scratch of at least ffa_bwd_workspace_size bytes, 256-byte aligned. */
+FFA_API ffa_status ffa_bwd(const ffa_shape* shape, ffa_tensor_in q, ffa_tensor_in k,
+                           ffa_tensor_in v, ffa_tensor_in o, const float* lse,
+                           ffa_tensor_in dout, const void* d_meta, ffa_tensor_out dq,
+                           ffa_tensor_out dk, ffa_tensor_out dv, void* d_ws, size_t ws_bytes,
+                           void* stream);
+
+/* Static description of a status code. */
+FFA_API const char* ffa_status_string(ffa_status status);
+
+/* FFA_ABI_VERSION of the built library. */
+FFA_API int32_t ffa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FFA_H_ */

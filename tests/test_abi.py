@@ -1,0 +1,101 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad host-visible arguments before enqueuing."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import flexible_mask_attention_amd as ffa
+from flexible_mask_attention_amd import workloads as wl
+from oracle import ffa_oracle as orc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ffa.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"FFA_API\s+[\w\s\*]+?\b(ffa_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_symbols()
+    assert len(names) == 8 and set(names) == set(ffa.EXPORTED)
+    L = ffa.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    # and nothing else with the ffa_ prefix is exported
+    out = os.popen(f"nm -D --defined-only {ffa.LIB_PATH}").read()
+    exported = sorted(set(re.findall(r"\b(ffa_\w+)\b", out)))
+    assert exported == names
+
+
+def test_abi_version_and_strings():
+    L = ffa.lib()
+    assert L.ffa_abi_version() == 1
+    for code in range(5):
+        assert len(L.ffa_status_string(code)) > 0
+
+
+def _shape(Tq=256, Tk=256, Hq=2, Hkv=2, d=64, scale=0.125):
+    return ffa.Shape(Tq, Tk, Hq, Hkv, d, scale)
+
+
+def test_host_validation_returns_before_enqueue():
+    L = ffa.lib()
+    good = ffa.TensorIn(0x1000, 128, 64)
+    goodo = ffa.TensorOut(0x1000, 128, 64)
+    meta = 0x10000
+    lse = 0x2000
+    P = ctypes.byref
+    # unsupported head_dim
+    assert L.ffa_fwd(P(_shape(d=96)), good, good, good, meta, goodo, lse, None) == 2
+    # Hq not a multiple of Hkv
+    assert L.ffa_fwd(P(_shape(Hq=3, Hkv=2)), good, good, good, meta, goodo, lse, None) == 1
+    # non-finite / zero scale
+    assert L.ffa_fwd(P(_shape(scale=float("nan"))), good, good, good, meta, goodo, lse, None) == 1
+    assert L.ffa_fwd(P(_shape(scale=0.0)), good, good, good, meta, goodo, lse, None) == 1
+    # null / misaligned tensor pointers, bad strides
+    assert L.ffa_fwd(P(_shape()), ffa.TensorIn(0, 128, 64), good, good, meta, goodo, lse, None) == 1
+    assert L.ffa_fwd(P(_shape()), ffa.TensorIn(0x1002, 128, 64), good, good, meta, goodo, lse, None) == 1
+    assert L.ffa_fwd(P(_shape()), ffa.TensorIn(0x1000, 129, 64), good, good, meta, goodo, lse, None) == 1
+    # misaligned metadata / lse
+    assert L.ffa_fwd(P(_shape()), good, good, good, meta + 16, goodo, lse, None) == 1
+    assert L.ffa_fwd(P(_shape()), good, good, good, meta, goodo, lse + 4, None) == 1
+    assert L.ffa_fwd(None, good, good, good, meta, goodo, lse, None) == 1
+    # backward workspace too small / null
+    ws = ctypes.c_size_t()
+    assert L.ffa_bwd_workspace_size(P(_shape()), P(ws)) == 0 and ws.value == 2 * 256 * 4
+    assert L.ffa_bwd(P(_shape()), good, good, good, good, lse, good, meta, goodo, goodo, goodo,
+                     0x100000, ws.value - 1, None) == 3
+    assert L.ffa_bwd(P(_shape()), good, good, good, good, lse, good, meta, goodo, goodo, goodo,
+                     None, ws.value, None) == 1
+    # metadata build: bad sizes, misaligned buffer, too-small buffer
+    n = ctypes.c_size_t()
+    assert L.ffa_block_meta_workspace_size(-1, 10, 10, 64, None, P(n)) == 1
+    assert L.ffa_block_meta_workspace_size(1, 10, 10, 80, None, P(n)) == 2
+    assert L.ffa_block_meta_workspace_size(1, 10, 10, 64, None, P(n)) == 0
+    assert L.ffa_build_block_meta(0x1000, 1, 10, 10, 64, 0x10010, n.value, None) == 1
+    assert L.ffa_build_block_meta(0x1000, 1, 10, 10, 64, 0x10000, 100, None) == 3
+    assert L.ffa_build_block_meta(0, 1, 10, 10, 64, 0x10000, n.value, None) == 1
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+def test_meta_workspace_bound_covers_actual_lists(idx):
+    """The host-side size bound must hold the exact CSR lists of the oracle."""
+    W = wl.workload(idx)
+    for c in W.calls[:1]:
+        host = torch.tensor(c.slices, dtype=torch.int32)
+        nbytes = ffa.meta_workspace_size(len(c.slices), c.Tq, c.Tk, c.d, host)
+        dense = ffa.meta_workspace_size(len(c.slices), c.Tq, c.Tk, c.d, None)
+        assert nbytes <= dense
+        qf = orc.block_meta(c.slices, c.Tq, c.Tk, 128, 64, "q2k")
+        kb = orc.block_meta(c.slices, c.Tq, c.Tk, 64, 128, "k2q")
+        entries = len(qf["full_block_idx"]) + len(qf["mask_block_idx"]) + \
+            len(kb["full_block_idx"]) + len(kb["mask_block_idx"])
+        nq = -(-c.Tq // 128)
+        nslices_lists = sum((s[1] - 1) // 128 - s[0] // 128 + 1 for s in c.slices if s[1] > s[0])
+        assert nbytes >= 4 * (entries + nslices_lists)

@@ -1,0 +1,284 @@
+"""FFA forward / backward on the GPU against the fp64 oracle.
+
+Tolerances (bf16 inputs, fp32 accumulation): O elementwise |d| <= 1e-2 + 1e-2|ref|;
+LSE |d| <= 1e-3 with -inf matching -inf; dQ, dK, dV relative Frobenius error
+<= 2e-2 over the checked rows.
+
+* small and medium cases (several tiles, ragged tails, every mask type, GQA,
+  both head dims): every output element against the oracle;
+* the 16K varlen-causal GQA workload: every element of O, LSE, dQ, dK, dV;
+* the 64K dense, 128K block-causal / sliding-window and 256K x 1M workloads at
+  full size, in the configuration the benchmark times: random inputs checked
+  on 4096 sampled query rows (O, LSE, dQ computed row by row by the oracle),
+  and structured inputs (equal keys, rank-1 values) whose exact O and LSE for
+  every row and dK, dV for 4096 sampled keys follow from interval sums
+  (tests/_props.py, pinned against the oracle in tests/test_props.py).
+"""
+import math
+import random
+
+import numpy as np
+import pytest
+import torch
+
+import flexible_mask_attention_amd as ffa
+from flexible_mask_attention_amd import workloads as wl
+from oracle import ffa_oracle as orc
+from tests import _props
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+# ------------------------------------------------------------- checks ----
+
+def check_o(got, ref, what="O"):
+    g = got.double().cpu().numpy()
+    err = np.abs(g - ref)
+    bad = err > 1e-2 + 1e-2 * np.abs(ref)
+    assert not bad.any(), f"{what}: {int(bad.sum())} of {bad.size} out of tolerance, max err {err.max():.3g}"
+
+
+def check_lse(got, ref, what="LSE"):
+    g = got.double().cpu().numpy()
+    assert np.array_equal(np.isneginf(g), np.isneginf(ref)), f"{what}: -inf pattern differs"
+    fin = np.isfinite(ref)
+    assert np.all(np.isfinite(g[fin]))
+    if fin.any():
+        err = np.abs(g[fin] - ref[fin]).max()
+        assert err <= 1e-3, f"{what}: max err {err:.3g}"
+
+
+def check_grad(got, ref, what):
+    g = got.double().cpu().numpy()
+    nr = np.linalg.norm(ref)
+    ne = np.linalg.norm(g - ref)
+    if nr == 0:
+        assert ne == 0, f"{what}: expected zero, got norm {ne:.3g}"
+        return
+    rel = ne / nr
+    assert rel <= 2e-2, f"{what}: relative Frobenius error {rel:.3g}"
+
+
+def run(call, T, meta=None, scale=None, bwd=True):
+    """GPU forward (+ backward) of one call; T holds q, k, v, do (any device)."""
+    q, k, v = (T[n].to(DEV) for n in ("q", "k", "v"))
+    meta = meta if meta is not None else ffa.build_meta(call.slices, call.Tq, call.Tk, call.d)
+    o, lse = ffa.fwd(q, k, v, meta, scale)
+    out = {"o": o, "lse": lse, "meta": meta}
+    if bwd:
+        do = T["do"].to(DEV)
+        dq, dk, dv = ffa.bwd(q, k, v, o, lse, do, meta, scale)
+        out.update(dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    return out
+
+
+def full_check(call, T, scale=None):
+    r = run(call, T, scale=scale)
+    assert r["meta"].status() == 0
+    o_ref, l_ref = orc.forward(T["q"], T["k"], T["v"], call.slices, scale)
+    check_o(r["o"], o_ref)
+    check_lse(r["lse"], l_ref)
+    dq, dk, dv = orc.backward(T["q"], T["k"], T["v"], T["do"], call.slices, scale)
+    check_grad(r["dq"], dq, "dQ")
+    check_grad(r["dk"], dk, "dK")
+    check_grad(r["dv"], dv, "dV")
+    return r
+
+
+# ---------------------------------------------------- small / medium ----
+
+@pytest.mark.parametrize("variant", ["causal", "mixed", "two_full"])
+def test_tiny_varlen(variant):
+    W = wl.tiny_varlen(variant)
+    c = W.calls[0]
+    _say(f"tiny varlen {variant}")
+    full_check(c, wl.make_tensors(c, W.seed))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_random_tables(d, seed):
+    rng = random.Random(seed * 10 + d)
+    Tq, Tk = rng.randint(300, 900), rng.randint(300, 900)
+    Hkv = rng.choice([1, 2])
+    Hq = Hkv * rng.choice([1, 2, 4])
+    sl = wl.random_slices(rng, Tq, Tk, rng.randint(2, 7))
+    c = wl.Call(sl, Tq, Tk, Hq, Hkv, d)
+    _say(f"random table seed={seed} d={d}: Tq={Tq} Tk={Tk} Hq={Hq} Hkv={Hkv} slices={sl}")
+    full_check(c, wl.make_tensors(c, 1000 + seed))
+
+
+def test_every_mask_type_lq_ne_lk():
+    sl = [(0, 100, 0, 300, wl.CAUSAL), (100, 300, 300, 400, wl.CAUSAL),        # Lq > Lk: empty first rows
+          (300, 450, 0, 200, wl.INV_CAUSAL), (450, 700, 400, 500, wl.INV_CAUSAL),
+          (700, 800, 500, 700, wl.BI_CAUSAL), (800, 900, 700, 750, wl.BI_CAUSAL),  # Lk < Lq: empty
+          (900, 1000, 750, 777, wl.FULL)]
+    c = wl.Call(sl, 1003, 777, 4, 2, 128)
+    full_check(c, wl.make_tensors(c, 7))
+
+
+def test_softmax_scale_and_strided_inputs():
+    c = wl.Call([(0, 200, 0, 260, wl.CAUSAL), (200, 333, 100, 300, wl.FULL)], 333, 300, 4, 2, 64)
+    T = wl.make_tensors(c, 8)
+    # q, k, v as views of packed buffers (non-contiguous head / token strides)
+    qkv = torch.zeros(c.Tq, 3 * c.Hq, c.d, dtype=torch.bfloat16)
+    qkv[:, :c.Hq] = T["q"]
+    kv = torch.zeros(c.Tk, 4 * c.Hkv, c.d, dtype=torch.bfloat16)
+    kv[:, :c.Hkv] = T["k"]
+    kv[:, 2 * c.Hkv:3 * c.Hkv] = T["v"]
+    qkv_d, kv_d = qkv.to(DEV), kv.to(DEV)
+    q, k, v = qkv_d[:, :c.Hq], kv_d[:, :c.Hkv], kv_d[:, 2 * c.Hkv:3 * c.Hkv]
+    meta = ffa.build_meta(c.slices, c.Tq, c.Tk, c.d)
+    scale = 0.37
+    o, lse = ffa.fwd(q, k, v, meta, scale)
+    dq, dk, dv = ffa.bwd(q, k, v, o, lse, T["do"].to(DEV), meta, scale)
+    o_ref, l_ref = orc.forward(T["q"], T["k"], T["v"], c.slices, scale)
+    check_o(o, o_ref)
+    check_lse(lse, l_ref)
+    gq, gk, gv = orc.backward(T["q"], T["k"], T["v"], T["do"], c.slices, scale)
+    check_grad(dq, gq, "dQ")
+    check_grad(dk, gk, "dK")
+    check_grad(dv, gv, "dV")
+
+
+def test_empty_table_and_rows_without_keys():
+    c = wl.Call([], 200, 150, 2, 1, 128)
+    T = wl.make_tensors(c, 9)
+    r = run(c, T)
+    assert (r["o"] == 0).all() and torch.isneginf(r["lse"]).all()
+    assert (r["dq"] == 0).all() and (r["dk"] == 0).all() and (r["dv"] == 0).all()
+    # a single short key range, most rows empty, Tk smaller than one key tile
+    c = wl.Call([(130, 140, 3, 20, wl.FULL)], 260, 20, 2, 2, 64)
+    full_check(c, wl.make_tensors(c, 10))
+
+
+def test_bad_table_writes_nothing():
+    c = wl.Call([(0, 64, 0, 64, 0), (32, 96, 60, 70, 0)], 128, 128, 2, 2, 64)   # overlap
+    T = wl.make_tensors(c, 11)
+    q, k, v = (T[n].to(DEV) for n in ("q", "k", "v"))
+    meta = ffa.build_meta(c.slices, c.Tq, c.Tk, c.d)
+    assert meta.status() == ffa.META_ERR_OVERLAP
+    o = torch.full_like(q, 7.0)
+    lse = torch.full((c.Hq, c.Tq), 7.0, device=DEV)
+    ffa.fwd(q, k, v, meta, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert (o == 7.0).all() and (lse == 7.0).all()
+
+
+# ------------------------------------------------ 16K varlen causal GQA ----
+
+_cache = {}
+
+
+def _cfg2():
+    if "cfg2" not in _cache:
+        W = wl.varlen_causal_gqa()
+        c = W.calls[0]
+        T = wl.make_tensors(c, W.seed)
+        _cache["cfg2"] = (c, T, run(c, T))
+    return _cache["cfg2"]
+
+
+def test_varlen_causal_gqa_forward_full():
+    c, T, r = _cfg2()
+    _say("16K varlen causal: oracle forward")
+    o_ref, l_ref = orc.forward(T["q"], T["k"], T["v"], c.slices)
+    check_o(r["o"], o_ref)
+    check_lse(r["lse"], l_ref)
+
+
+def test_varlen_causal_gqa_backward_full():
+    c, T, r = _cfg2()
+    _say("16K varlen causal: oracle backward")
+    dq, dk, dv = orc.backward(T["q"], T["k"], T["v"], T["do"], c.slices)
+    check_grad(r["dq"], dq, "dQ")
+    check_grad(r["dk"], dk, "dK")
+    check_grad(r["dv"], dv, "dV")
+
+
+def test_determinism_and_table_invariance():
+    c, T, r = _cfg2()
+    r2 = run(c, T)
+    for key in ("o", "lse", "dq", "dk", "dv"):
+        assert torch.equal(r[key], r2[key]), key
+    # the same mask written as a permuted and split table gives identical bits
+    sl = list(reversed(c.slices))
+    q0, q1, k0, k1, t = sl[0]
+    mid = (q0 + q1) // 2
+    sl = [(q0, mid, k0, mid, wl.CAUSAL), (mid, q1, k0, mid, wl.FULL), (mid, q1, mid, q1, wl.CAUSAL)] + sl[1:]
+    c2 = wl.Call(sl, c.Tq, c.Tk, c.Hq, c.Hkv, c.d)
+    r3 = run(c2, T)
+    for key in ("o", "lse", "dq", "dk", "dv"):
+        assert torch.equal(r[key], r3[key]), key
+
+
+# ----------------------------------------------------- full-size cases ----
+
+LARGE = [(3, 0), (4, 0), (4, 1), (5, 0)]
+
+
+def _gpu_inputs(c, seed):
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    shp = {"q": (c.Tq, c.Hq, c.d), "k": (c.Tk, c.Hkv, c.d), "v": (c.Tk, c.Hkv, c.d), "do": (c.Tq, c.Hq, c.d)}
+    return {n: torch.randn(*shp[n], generator=g, device=DEV).to(torch.bfloat16) for n in ("q", "k", "v", "do")}
+
+
+@pytest.mark.parametrize("idx,call", LARGE)
+@pytest.mark.parametrize("part", [0, 1])
+def test_large_sampled_rows(idx, call, part):
+    """Random N(0,1) inputs at full size; 4096 sampled rows (two halves) per workload."""
+    W = wl.workload(idx)
+    c = W.calls[call]
+    key = ("rand", idx, call)
+    if key not in _cache:
+        _cache.clear()
+        _say(f"workload {idx} call {call}: random inputs, GPU fwd+bwd")
+        T = _gpu_inputs(c, 100 * idx + call)
+        r = run(c, T)
+        Tc = {n: t.cpu() for n, t in T.items()}
+        res = {n: r[n].cpu() for n in ("o", "lse", "dq")}
+        del T, r
+        torch.cuda.empty_cache()
+        _cache[key] = (Tc, res)
+    Tc, res = _cache[key]
+    rows = np.sort(np.random.default_rng(100 + idx).choice(c.Tq, 4096, replace=False))
+    rows = rows[part::2]
+    _say(f"workload {idx} call {call} part {part}: oracle on {len(rows)} rows")
+    O, L, dQ = orc.forward_backward_rows(Tc["q"], Tc["k"], Tc["v"], Tc["do"], c.slices, rows)
+    check_o(res["o"][rows], O)
+    check_lse(res["lse"][:, rows], L)
+    check_grad(res["dq"][rows], dQ, "dQ")
+
+
+@pytest.mark.parametrize("idx,call", LARGE)
+def test_large_structured(idx, call):
+    """Equal keys and rank-1 values at full size: exact O, LSE for every row,
+    dK, dV for 4096 sampled keys, and V = 1 gives O = 1 on non-empty rows."""
+    W = wl.workload(idx)
+    c = W.calls[call]
+    _cache.clear()
+    _say(f"workload {idx} call {call}: structured inputs")
+    inp = _props.structured_inputs(c.Tq, c.Tk, c.Hq, c.Hkv, c.d, 500 + idx, device=DEV)
+    r = run(c, inp)
+    o, lse, dk, dv = (r[n].cpu() for n in ("o", "lse", "dk", "dv"))
+    ones = {"q": inp["q"], "k": inp["k"], "v": torch.ones_like(inp["v"]), "do": inp["do"]}
+    o1 = run(c, ones, meta=r["meta"], bwd=False)["o"].cpu()
+    del r
+    st = _props.Structured(inp, c.slices, c.Tq, c.Tk)
+    for h in range(c.Hq):
+        O, L = st.rows(h)
+        check_o(o[:, h], O, f"O head {h}")
+        check_lse(lse[h], L, f"LSE head {h}")
+        want1 = np.where(st.nz[:, None], 1.0, 0.0) * np.ones((1, c.d))
+        check_o(o1[:, h], want1, f"O (V=1) head {h}")
+    keys = np.sort(np.random.default_rng(200 + idx).choice(c.Tk, 4096, replace=False))
+    for g in range(c.Hkv):
+        dK, dV = st.keys(g, keys)
+        check_grad(dk[keys, g], dK, f"dK head {g}")
+        check_grad(dv[keys, g], dV, f"dV head {g}")

@@ -1,0 +1,116 @@
+"""Block metadata on the GPU must equal the oracle's bit for bit (integer work)."""
+import random
+
+import numpy as np
+import pytest
+import torch
+
+import flexible_mask_attention_amd as ffa
+from flexible_mask_attention_amd import workloads as wl
+from oracle import ffa_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _expected_slice_lists(slices, Tq, Tk, BM):
+    nq = -(-Tq // BM)
+    out = [[] for _ in range(nq)]
+    for i, (q0, q1, k0, k1, t) in enumerate(slices):
+        if not (0 <= q0 <= q1 <= Tq and 0 <= k0 <= k1 <= Tk and 0 <= t <= 3):
+            continue
+        if q1 <= q0 or k1 <= k0:
+            continue
+        for m in range(q0 // BM, (q1 - 1) // BM + 1):
+            out[m].append(i)
+    return out
+
+
+def check_meta(slices, Tq, Tk, d=128, meta=None):
+    m = meta if meta is not None else ffa.build_meta(slices, Tq, Tk, d)
+    csr = m.csr()
+    BMf, BNf, BMb, BNb = csr["tiles"]
+    assert m.status() == orc.validate(slices, Tq, Tk)
+    if m.status():
+        return m, csr
+    assert m.area() == orc.total_area(slices)
+    for direction, (BM, BN) in (("q2k", (BMf, BNf)), ("k2q", (BMb, BNb))):
+        ref = orc.block_meta(slices, Tq, Tk, BM, BN, direction)
+        got = csr[direction]
+        for key in ("full_block_offset", "full_block_idx", "mask_block_offset", "mask_block_idx"):
+            assert np.array_equal(got[key].numpy(), ref[key]), (direction, key)
+    lists = _expected_slice_lists(slices, Tq, Tk, BMf)
+    qs_off, qs_idx = csr["qblock_slice_offset"].numpy(), csr["qblock_slice_idx"].numpy()
+    for mblk, want in enumerate(lists):
+        assert list(qs_idx[qs_off[mblk]:qs_off[mblk + 1]]) == want
+    for sched, which in ((csr["schedule_fwd"], "q2k"), (csr["schedule_bwd"], "k2q")):
+        s = sched.numpy()
+        assert sorted(s.tolist()) == list(range(len(s)))
+        fo = csr[which]["full_block_offset"].numpy()
+        mo = csr[which]["mask_block_offset"].numpy()
+        cost = 4 * np.diff(fo) + 5 * np.diff(mo)
+        assert np.all(np.diff(cost[s]) <= 0)
+    return m, csr
+
+
+@pytest.mark.parametrize("variant", ["causal", "mixed", "two_full"])
+def test_meta_tiny(variant):
+    c = wl.tiny_varlen(variant).calls[0]
+    check_meta(c.slices, c.Tq, c.Tk, c.d)
+
+
+@pytest.mark.parametrize("idx,call", [(2, 0), (3, 0), (4, 0), (4, 1), (5, 0)])
+def test_meta_workloads(idx, call):
+    c = wl.workload(idx).calls[call]
+    _say(f"meta parity: workload {idx} call {call}: {len(c.slices)} slices, Tq={c.Tq} Tk={c.Tk}")
+    check_meta(c.slices, c.Tq, c.Tk, c.d)
+
+
+def test_meta_random_tables():
+    rng = random.Random(1234)
+    for trial in range(40):
+        Tq, Tk = rng.randint(1, 700), rng.randint(1, 700)
+        n = rng.randint(1, min(8, Tq))
+        sl = wl.random_slices(rng, Tq, Tk, n) if Tq > 1 else [(0, 1, 0, Tk, rng.randint(0, 3))]
+        _say(f"random table {trial}: Tq={Tq} Tk={Tk} n={len(sl)}")
+        check_meta(sl, Tq, Tk, rng.choice([64, 128]))
+
+
+def test_meta_multi_slice_tiles_and_empty():
+    # several slices share tiles; zero-area slices; a BI_CAUSAL with Lk < Lq (empty)
+    sl = [(0, 50, 0, 30, wl.CAUSAL), (0, 50, 30, 90, wl.FULL), (50, 70, 10, 15, wl.BI_CAUSAL),
+          (70, 70, 0, 10, wl.FULL), (70, 200, 90, 91, wl.INV_CAUSAL), (200, 333, 0, 300, wl.BI_CAUSAL)]
+    check_meta(sl, 333, 300)
+    check_meta([], 100, 100)
+
+
+def test_meta_invariant_under_permutation_and_splitting():
+    sl = [(0, 40, 0, 40, 1), (40, 100, 10, 90, 0), (100, 150, 60, 170, 3), (150, 200, 0, 30, 2)]
+    split = [(0, 17, 0, 17, 1), (17, 40, 0, 17, 0), (17, 40, 17, 40, 1), (40, 70, 10, 90, 0),
+             (70, 100, 10, 50, 0), (70, 100, 50, 90, 0), (100, 150, 60, 170, 3), (150, 200, 0, 30, 2)]
+    _, a = check_meta(sl, 200, 170)
+    _, b = check_meta(list(reversed(sl)), 200, 170)
+    _, c = check_meta(split, 200, 170)
+    for other in (b, c):
+        for direction in ("q2k", "k2q"):
+            for key in a[direction]:
+                assert torch.equal(a[direction][key], other[direction][key])
+
+
+def test_meta_status_flags():
+    assert check_meta([(0, 10, 0, 10, 0), (5, 15, 9, 12, 0)], 20, 20)[0].status() == ffa.META_ERR_OVERLAP
+    assert check_meta([(0, 8, 0, 8, 1), (0, 8, 0, 8, 2)], 8, 8)[0].status() == ffa.META_ERR_OVERLAP
+    assert check_meta([(0, 21, 0, 10, 1)], 20, 20)[0].status() == ffa.META_ERR_BOUNDS
+    assert check_meta([(3, 2, 0, 10, 1)], 20, 20)[0].status() == ffa.META_ERR_BOUNDS
+    assert check_meta([(0, 10, 0, 10, 9)], 20, 20)[0].status() == ffa.META_ERR_TYPE
+    # a buffer too small for the lists sets the capacity flag (and nothing is written past it)
+    sl = wl.varlen_causal_gqa().calls[0].slices
+    need = ffa.meta_workspace_size(len(sl), 16384, 16384, 128, torch.tensor(sl, dtype=torch.int32))
+    fixed = ffa.meta_workspace_size(len(sl), 16384, 16384, 128, torch.zeros(len(sl), 5, dtype=torch.int32))
+    guard = torch.full((need + 4096,), 0x5A, dtype=torch.uint8, device="cuda")
+    m = ffa.build_meta(sl, 16384, 16384, 128, out=guard[:fixed + 256])
+    assert m.status() & ffa.META_ERR_CAPACITY
+    assert bool((guard[fixed + 256:] == 0x5A).all())

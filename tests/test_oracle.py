@@ -54,6 +54,9 @@ def test_row_and_col_intervals_match_predicate(t):
                 iv = orc.col_interval(s, j)
                 got = [] if iv is None else list(range(iv[0], iv[1] + 1))
                 assert got == want, (s, j)
+                lo, hi, ok = orc.col_intervals_vec(s, np.array([j]))
+                got_v = list(range(lo[0], hi[0] + 1)) if ok[0] else []
+                assert got_v == want
 
 
 def test_dense_mask_matches_predicate():
