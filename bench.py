@@ -1,0 +1,204 @@
+#!/usr/bin/env python3
+"""Benchmark: Flex-Flash-Attention forward + backward TFLOP/s on one MI355X.
+
+One step is one pass of the whole hot path over resident synthetic inputs:
+block metadata of the slice table, forward (O, LSE) and backward (dQ, dK, dV).
+FLOPs follow the MagiAttention blog deep-dive ("训练和 Benchmark 设置", FLOPs
+equation): FLOPs_fwd = 4 * d * MaskArea * Hq, FLOPs_bwd = 2.5 * FLOPs_fwd,
+MaskArea being the exact valid-pair count (computed on the device by the
+metadata kernels); throughput = FLOPs / elapsed time (documentation page,
+throughput formulas).
+
+Default workload: 16384-token varlen-causal GQA (Hq 32, Hkv 8, d 128), lengths
+U[256, 4096] trimmed to the total, seed 2.  Prints one JSON line.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import flexible_mask_attention_amd as ffa  # noqa: E402
+from flexible_mask_attention_amd import workloads as wl  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+METRIC = "FFA fwd/bwd TFLOPs/s on valid mask area at 1 MI355X; % of bf16 MFMA peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Case:
+    """Resident inputs, outputs and scratch of one library call."""
+
+    def __init__(self, call, seed, dev):
+        self.c = call
+        g = torch.Generator(device=dev).manual_seed(seed)
+        shp = {"q": (call.Tq, call.Hq, call.d), "k": (call.Tk, call.Hkv, call.d),
+               "v": (call.Tk, call.Hkv, call.d), "do": (call.Tq, call.Hq, call.d)}
+        for n in ("q", "k", "v", "do"):
+            setattr(self, n, torch.randn(*shp[n], generator=g, device=dev).to(torch.bfloat16))
+        host = torch.tensor(call.slices, dtype=torch.int32).reshape(-1, 5)
+        self.slices = host.to(dev)
+        nbytes = ffa.meta_workspace_size(len(call.slices), call.Tq, call.Tk, call.d, host)
+        self.meta_buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self.meta = ffa.build_meta(self.slices, call.Tq, call.Tk, call.d, out=self.meta_buf)
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty(call.Hq, call.Tq, dtype=torch.float32, device=dev)
+        self.dq, self.dk, self.dv = torch.empty_like(self.q), torch.empty_like(self.k), torch.empty_like(self.v)
+        self.ws = torch.empty(max(256, ffa.bwd_workspace_size(self.q, self.k)), dtype=torch.uint8, device=dev)
+
+    def build_meta(self):
+        c = self.c
+        ffa._check(ffa.lib().ffa_build_block_meta(self.slices.data_ptr(), len(c.slices), c.Tq, c.Tk, c.d,
+                                                  self.meta_buf.data_ptr(), self.meta_buf.numel(),
+                                                  ffa._stream()), "ffa_build_block_meta")
+
+    def fwd(self):
+        ffa.fwd(self.q, self.k, self.v, self.meta, out=self.o, lse=self.lse)
+
+    def bwd(self, phases=ffa.BWD_ALL):
+        ffa.bwd(self.q, self.k, self.v, self.o, self.lse, self.do, self.meta, dq=self.dq, dk=self.dk,
+                dv=self.dv, workspace=self.ws, phases=phases)
+
+    def step(self):
+        self.build_meta()
+        self.fwd()
+        self.bwd()
+
+
+def phase_times(cases, reps):
+    """Average device time (ms) of each phase, from HIP events on the stream the
+    library launches on (torch's current stream)."""
+    names = ["meta", "fwd", "bwd_pre", "bwd_dkdv", "bwd_dq"]
+    tot = {n: 0.0 for n in names}
+    for _ in range(reps):
+        for cs in cases:
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+            ev[0].record()
+            cs.build_meta()
+            ev[1].record()
+            cs.fwd()
+            ev[2].record()
+            cs.bwd(ffa.BWD_PRE)
+            ev[3].record()
+            cs.bwd(ffa.BWD_DKDV)
+            ev[4].record()
+            cs.bwd(ffa.BWD_DQ)
+            ev[5].record()
+            torch.cuda.synchronize()
+            for i, n in enumerate(names):
+                tot[n] += ev[i].elapsed_time(ev[i + 1])
+    return {n: tot[n] / reps for n in names}
+
+
+def cpu_baseline(call, seed, area, min_seconds=10.0):
+    """The fp64 oracle, untuned, timed on the host cores: forward + backward of
+    the whole workload (all heads, full mask), repeated until at least
+    ``min_seconds`` have passed.  Inputs are the CPU-seeded tensors of the
+    same shapes."""
+    from oracle import ffa_oracle as orc
+    T = wl.make_tensors(call, seed)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        orc.forward(T["q"], T["k"], T["v"], call.slices)
+        orc.backward(T["q"], T["k"], T["v"], T["do"], call.slices)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or reps >= 5:
+            break
+    f = 4.0 * call.d * area * call.Hq * 3.5 * reps
+    return {"value": round(f / dt / 1e12, 4), "unit": "TFLOP/s", "cores": torch.get_num_threads(),
+            "kind": "oracle",
+            "sample": f"whole workload (all {call.Hq} query heads, full mask), fwd + bwd, "
+                      f"{reps} pass(es) in {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2, help="1..5 (see workloads.py)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        log("bench.py measures one GPU only: this library has no multi-GPU path "
+            "(each GPU would run its own share of the slices unchanged).")
+        sys.exit(2)
+
+    dev = torch.device("cuda:0")
+    W = wl.workload(args.workload)
+    cases = [Case(c, 100 * W.seed + i, dev) for i, c in enumerate(W.calls)]
+    torch.cuda.synchronize()
+    areas = [cs.meta.area() for cs in cases]
+    for cs in cases:
+        assert cs.meta.status() == 0
+    f_fwd = sum(4.0 * cs.c.d * a * cs.c.Hq for cs, a in zip(cases, areas))
+    f_bwd = 2.5 * f_fwd
+
+    for _ in range(args.warmup):
+        for cs in cases:
+            cs.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for cs in cases:
+            cs.step()
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / args.steps
+
+    ph = phase_times(cases, max(5, args.steps // 2))
+    t_fwd = ph["fwd"] * 1e-3
+    t_bwd = (ph["bwd_pre"] + ph["bwd_dkdv"] + ph["bwd_dq"]) * 1e-3
+    # algorithmic FLOPs per kernel: fwd 4d per valid pair and head; of the
+    # backward's 10d, dK/dV take 8d (Q K^T, dO V^T, P^T dO, dS^T Q), dQ 2d (dS K)
+    alg = {"fwd": f_fwd, "bwd_dkdv": 0.8 * f_bwd, "bwd_dq": 0.2 * f_bwd}
+    kernels = {}
+    for n in ("fwd", "bwd_dkdv", "bwd_dq"):
+        tf = alg[n] / (ph[n] * 1e-3) / 1e12
+        kernels[n] = {"ms": round(ph[n], 4), "tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+    pre_bytes = sum(cs.c.Tq * cs.c.Hq * (2 * 2 * cs.c.d + 4) for cs in cases)
+    kernels["bwd_pre"] = {"ms": round(ph["bwd_pre"], 4),
+                          "gbs": round(pre_bytes / (ph["bwd_pre"] * 1e-3) / 1e9, 1)}
+    kernels["meta"] = {"ms": round(ph["meta"], 4)}
+    dom = max(("fwd", "bwd_dkdv", "bwd_dq"), key=lambda n: ph[n])
+    achieved = kernels[dom]["tflops"]
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+
+    value = (f_fwd + f_bwd) / step_s / 1e12
+    c0 = W.calls[0]
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": W.name, "seqlen_q": c0.Tq, "seqlen_k": c0.Tk,
+                   "num_heads_q": sum(c.Hq for c in W.calls), "num_heads_kv": sum(c.Hkv for c in W.calls),
+                   "head_dim": c0.d, "num_slices": sum(len(c.slices) for c in W.calls),
+                   "mask_area": sum(areas), "flops_fwd": f_fwd, "flops_bwd": f_bwd, "seed": W.seed,
+                   "step": "block metadata + forward + backward"},
+        "fwd_tflops": round(f_fwd / t_fwd / 1e12, 1),
+        "fwd_pct_peak": round(100 * f_fwd / t_fwd / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "bwd_tflops": round(f_bwd / t_bwd / 1e12, 1),
+        "bwd_pct_peak": round(100 * f_bwd / t_bwd / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "kernels": kernels,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on a bounded sample ...")
+        out["cpu_baseline"] = cpu_baseline(c0, W.seed, areas[0])
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

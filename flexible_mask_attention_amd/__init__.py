@@ -26,8 +26,9 @@ META_ERR_BOUNDS, META_ERR_TYPE, META_ERR_OVERLAP, META_ERR_CAPACITY = 1, 2, 4, 8
 
 EXPORTED = (
     "ffa_block_meta_workspace_size", "ffa_build_block_meta", "ffa_block_meta_view", "ffa_fwd",
-    "ffa_bwd_workspace_size", "ffa_bwd", "ffa_status_string", "ffa_abi_version",
+    "ffa_bwd_workspace_size", "ffa_bwd", "ffa_bwd_phases", "ffa_status_string", "ffa_abi_version",
 )
+BWD_PRE, BWD_DKDV, BWD_DQ, BWD_ALL = 1, 2, 4, 7
 
 
 class FFAError(RuntimeError):
@@ -85,6 +86,8 @@ def lib() -> ctypes.CDLL:
     L.ffa_bwd.argtypes = [ctypes.POINTER(Shape), TensorIn, TensorIn, TensorIn, TensorIn, vp, TensorIn,
                           vp, TensorOut, TensorOut, TensorOut, vp, sz, vp]
     L.ffa_bwd.restype = st
+    L.ffa_bwd_phases.argtypes = L.ffa_bwd.argtypes[:-1] + [i32, vp]
+    L.ffa_bwd_phases.restype = st
     L.ffa_status_string.argtypes = [st]
     L.ffa_status_string.restype = ctypes.c_char_p
     L.ffa_abi_version.argtypes = []
@@ -243,8 +246,9 @@ def bwd_workspace_size(q, k, scale=None) -> int:
 
 
 def bwd(q, k, v, o, lse, do, meta: BlockMeta, scale: float = None, dq=None, dk=None, dv=None,
-        workspace: Optional[torch.Tensor] = None, stream=None):
-    """Backward -> (dq, dk, dv), bf16, same shapes as q, k, v."""
+        workspace: Optional[torch.Tensor] = None, stream=None, phases: int = BWD_ALL):
+    """Backward -> (dq, dk, dv), bf16, same shapes as q, k, v.  ``phases``
+    selects a subset of the backward kernels (BWD_PRE | BWD_DKDV | BWD_DQ)."""
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
         _check_thd(t, n)
     sh = _shape(q, k, scale)
@@ -254,9 +258,9 @@ def bwd(q, k, v, o, lse, do, meta: BlockMeta, scale: float = None, dq=None, dk=N
     need = bwd_workspace_size(q, k, scale)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    _check(lib().ffa_bwd(ctypes.byref(sh), _tin(q), _tin(k), _tin(v), _tin(o), lse.data_ptr(), _tin(do),
-                         meta.ptr, _tout(dq), _tout(dk), _tout(dv), workspace.data_ptr(),
-                         workspace.numel(), _stream(stream)), "ffa_bwd")
+    _check(lib().ffa_bwd_phases(ctypes.byref(sh), _tin(q), _tin(k), _tin(v), _tin(o), lse.data_ptr(),
+                                _tin(do), meta.ptr, _tout(dq), _tout(dk), _tout(dv), workspace.data_ptr(),
+                                workspace.numel(), int(phases), _stream(stream)), "ffa_bwd_phases")
     return dq, dk, dv
 
 
@@ -280,6 +284,6 @@ def ffa_attention(q, k, v, meta: BlockMeta, scale: float = None) -> torch.Tensor
     return FFAFunction.apply(q, k, v, meta, scale)
 
 
-__all__ = ["build_meta", "fwd", "bwd", "ffa_attention", "FFAFunction", "BlockMeta", "lib",
+__all__ = ["BWD_PRE", "BWD_DKDV", "BWD_DQ", "BWD_ALL", "build_meta", "fwd", "bwd", "ffa_attention", "FFAFunction", "BlockMeta", "lib",
            "meta_workspace_size", "bwd_workspace_size", "FFAError", "FULL", "CAUSAL", "INV_CAUSAL",
            "BI_CAUSAL", "EXPORTED"]

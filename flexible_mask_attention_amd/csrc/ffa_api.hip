@@ -180,6 +180,16 @@ FFA_API ffa_status ffa_bwd(const ffa_shape* shape, ffa_tensor_in q, ffa_tensor_i
                            ffa_tensor_in dout, const void* d_meta, ffa_tensor_out dq,
                            ffa_tensor_out dk, ffa_tensor_out dv, void* d_ws, size_t ws_bytes,
                            void* stream) {
+  return ffa_bwd_phases(shape, q, k, v, o, lse, dout, d_meta, dq, dk, dv, d_ws, ws_bytes,
+                        FFA_BWD_ALL, stream);
+}
+
+FFA_API ffa_status ffa_bwd_phases(const ffa_shape* shape, ffa_tensor_in q, ffa_tensor_in k,
+                                  ffa_tensor_in v, ffa_tensor_in o, const float* lse,
+                                  ffa_tensor_in dout, const void* d_meta, ffa_tensor_out dq,
+                                  ffa_tensor_out dk, ffa_tensor_out dv, void* d_ws,
+                                  size_t ws_bytes, int32_t phases, void* stream) {
+  if (phases & ~FFA_BWD_ALL) return FFA_ERR_INVALID_ARGUMENT;
   ffa_status st = check_shape(shape);
   if (st != FFA_OK) return st;
   const int D = shape->head_dim, Tq = shape->seqlen_q, Tk = shape->seqlen_k;
@@ -235,7 +245,7 @@ FFA_API ffa_status ffa_bwd(const ffa_shape* shape, ffa_tensor_in q, ffa_tensor_i
   a.Hkv = Hkv;
   a.scale = shape->softmax_scale;
   a.scale_log2 = shape->softmax_scale * LOG2E;
-  hipError_t e = launch_bwd(a, D, L.nq_f, L.nk_b, reinterpret_cast<hipStream_t>(stream));
+  hipError_t e = launch_bwd(a, D, L.nq_f, L.nk_b, phases, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? FFA_OK : FFA_ERR_HIP;
 }
 

@@ -438,16 +438,17 @@ __global__ __launch_bounds__(NT, 1) void ffa_bwd_dq_kernel(BwdArgs a) {
 
 }  // namespace
 
-hipError_t launch_bwd(const BwdArgs& a, int head_dim, int nq_f, int nk_b, hipStream_t stream) {
+hipError_t launch_bwd(const BwdArgs& a, int head_dim, int nq_f, int nk_b, int phases,
+                      hipStream_t stream) {
   const int64_t rows = (int64_t)a.Tq * a.Hq;
-  if (rows > 0) {
+  if ((phases & FFA_BWD_PRE) && rows > 0) {
     const int G = head_dim / 8;
     const int64_t blocks = (rows * G + NT - 1) / NT;
     if (head_dim == 128) ffa_bwd_pre_kernel<128><<<dim3((unsigned)blocks), NT, 0, stream>>>(a);
     else ffa_bwd_pre_kernel<64><<<dim3((unsigned)blocks), NT, 0, stream>>>(a);
   }
   const int64_t gk = (int64_t)nk_b * a.Hkv;
-  if (gk > 0) {
+  if ((phases & FFA_BWD_DKDV) && gk > 0) {
     if (head_dim == 128) {
       const size_t lds = 2 * (2 * BM_B * 128 * 2 + 2 * BM_B * 4);
       ffa_bwd_dkdv_kernel<128><<<dim3((unsigned)gk), NT, lds, stream>>>(a);
@@ -457,7 +458,7 @@ hipError_t launch_bwd(const BwdArgs& a, int head_dim, int nq_f, int nk_b, hipStr
     }
   }
   const int64_t gq = (int64_t)nq_f * a.Hq;
-  if (gq > 0) {
+  if ((phases & FFA_BWD_DQ) && gq > 0) {
     if (head_dim == 128) {
       const size_t lds = 2 * 2 * BN_F * 128 * 2;
       ffa_bwd_dq_kernel<128><<<dim3((unsigned)gq), NT, lds, stream>>>(a);

@@ -302,6 +302,7 @@ struct BwdArgs {
   float scale_log2;
   float scale;
 };
-hipError_t launch_bwd(const BwdArgs& a, int head_dim, int nq_f, int nk_b, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, int head_dim, int nq_f, int nk_b, int phases,
+                      hipStream_t stream);
 
 }  // namespace ffa

@@ -179,6 +179,23 @@ FFA_API ffa_status ffa_bwd(const ffa_shape* shape, ffa_tensor_in q, ffa_tensor_i
                            ffa_tensor_out dk, ffa_tensor_out dv, void* d_ws, size_t ws_bytes,
                            void* stream);
 
+/* Phases of the backward, for ffa_bwd_phases. */
+#define FFA_BWD_PRE 1   /* D_i = dO_i . O_i into d_ws                           */
+#define FFA_BWD_DKDV 2  /* dk, dv (reads D from d_ws)                             */
+#define FFA_BWD_DQ 4    /* dq (reads D from d_ws)                                 */
+#define FFA_BWD_ALL 7
+
+/* ffa_bwd restricted to a subset of its phases (bitwise OR of FFA_BWD_*), in
+ * the order PRE, DKDV, DQ.  DKDV and DQ read the D values that PRE wrote into
+ * the same d_ws; DKDV and DQ are independent of each other, so a caller may
+ * run them on two streams once PRE has finished.  phases = FFA_BWD_ALL is
+ * ffa_bwd.  Unknown bits give FFA_ERR_INVALID_ARGUMENT. */
+FFA_API ffa_status ffa_bwd_phases(const ffa_shape* shape, ffa_tensor_in q, ffa_tensor_in k,
+                                  ffa_tensor_in v, ffa_tensor_in o, const float* lse,
+                                  ffa_tensor_in dout, const void* d_meta, ffa_tensor_out dq,
+                                  ffa_tensor_out dk, ffa_tensor_out dv, void* d_ws,
+                                  size_t ws_bytes, int32_t phases, void* stream);
+
 /* Static description of a status code. */
 FFA_API const char* ffa_status_string(ffa_status status);
 

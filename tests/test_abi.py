@@ -23,7 +23,7 @@ def declared_symbols():
 
 def test_exports_every_declared_symbol():
     names = declared_symbols()
-    assert len(names) == 8 and set(names) == set(ffa.EXPORTED)
+    assert len(names) == 9 and set(names) == set(ffa.EXPORTED)
     L = ffa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -73,6 +73,8 @@ def test_host_validation_returns_before_enqueue():
                      0x100000, ws.value - 1, None) == 3
     assert L.ffa_bwd(P(_shape()), good, good, good, good, lse, good, meta, goodo, goodo, goodo,
                      None, ws.value, None) == 1
+    assert L.ffa_bwd_phases(P(_shape()), good, good, good, good, lse, good, meta, goodo, goodo, goodo,
+                            0x100000, ws.value, 8, None) == 1
     # metadata build: bad sizes, misaligned buffer, too-small buffer
     n = ctypes.c_size_t()
     assert L.ffa_block_meta_workspace_size(-1, 10, 10, 64, None, P(n)) == 1
