@@ -36,8 +36,9 @@ bool check_tensor(const void* p, int64_t ts, int64_t hs, int64_t T, int64_t H, i
   if (T == 0) return true;
   if (!p || !aligned(p, 16)) return false;
   if (ts < 0 || hs < 0 || ts % 8 || hs % 8) return false;
+  // tiles are read through buffer descriptors spanning up to 128 token rows
+  if (T > 1 && (ts < D || ts >= (1LL << 23))) return false;
   (void)H;
-  (void)D;
   return true;
 }
 
@@ -47,7 +48,7 @@ ffa_status check_shape(const ffa_shape* s) {
     return FFA_ERR_INVALID_ARGUMENT;
   if (s->num_heads_q % s->num_heads_kv) return FFA_ERR_INVALID_ARGUMENT;
   if (s->head_dim != 64 && s->head_dim != 128) return FFA_ERR_UNSUPPORTED;
-  if (!std::isfinite(s->softmax_scale) || s->softmax_scale == 0.f) return FFA_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(s->softmax_scale) || !(s->softmax_scale > 0.f)) return FFA_ERR_INVALID_ARGUMENT;
   return FFA_OK;
 }
 

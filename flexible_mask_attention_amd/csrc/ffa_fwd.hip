@@ -14,6 +14,8 @@
 // feed the next MFMA (O^T += V^T P^T) directly as its B operand; V^T comes
 // from LDS through ds_read_b64_tr_b16.  K and V tiles are double-buffered in
 // LDS; global loads for tile t+1 are issued before tile t is computed.
+#include <type_traits>
+
 #include "ffa_internal.hpp"
 
 namespace ffa {
@@ -26,8 +28,7 @@ template <int D>
 __global__ __launch_bounds__(NT, 2) void ffa_fwd_kernel(FwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int TILE_B = BN_F * D * 2;          // bytes of one K or V tile
-  constexpr int NCH = D / 8;                    // 16-byte chunks per row
-  constexpr int PERT = BN_F * NCH / NT;         // chunks per thread per tile
+  constexpr int STAGE_B = 2 * TILE_B;
   constexpr int KB = BN_F / 32;                 // 32-key blocks per tile
   constexpr int MB = D / 32;                    // 32-wide d blocks of O^T
   constexpr int KS = D / 16;                    // 16-wide d steps of S^T
@@ -36,7 +37,8 @@ __global__ __launch_bounds__(NT, 2) void ffa_fwd_kernel(FwdArgs a) {
   const MetaHeader* hd = mv.hdr;
   if (hd->status != 0 || hd->seqlen_q != a.Tq || hd->seqlen_k != a.Tk) return;
 
-  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int l32 = lane & 31, h32 = lane >> 5, t16 = lane & 15, g16 = lane >> 4;
   const int head = blockIdx.x % a.Hq;
   const int m = mv.sched_f[blockIdx.x / a.Hq];
@@ -63,80 +65,71 @@ __global__ __launch_bounds__(NT, 2) void ffa_fwd_kernel(FwdArgs a) {
     }
   }
 
+  // loop-invariant LDS read addresses (stage, key block and chunk offsets
+  // are added as immediates)
+  int kaddr[KS];
+#pragma unroll
+  for (int k = 0; k < KS; ++k) kaddr[k] = lds_off<D>(l32, 2 * k + h32);
+  int vaddr[MB][2];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int rr = 4 * h32 + (t16 >> 2) + 8 * j;
+      const int cc = 32 * mb + 16 * (g16 & 1) + 4 * (t16 & 3);
+      vaddr[mb][j] = lds_off<D>(rr, cc >> 3) + ((cc & 7) << 1);
+    }
+
+  TileDma<D, BN_F> dma;
+  dma.init(wid, lane, a.k_ts);
+  TileDma<D, BN_F> dmv;
+  dmv.init(wid, lane, a.v_ts);
+  const __bf16* kbase = a.k + (int64_t)kvh * a.k_hs;
+  const __bf16* vbase = a.v + (int64_t)kvh * a.v_hs;
+  auto tile_of = [&](int t) { return t < nP ? pidx[t] : fidx[t - nP]; };
+  auto issue = [&](int t, int stage) {
+    const int n = tile_of(t);
+    char* st = smem + stage * STAGE_B;
+    dma.load(kbase, a.k_ts, n * BN_F, a.Tk - n * BN_F, st);
+    dmv.load(vbase, a.v_ts, n * BN_F, a.Tk - n * BN_F, st + TILE_B);
+  };
+
   f32x16 oacc[MB];
 #pragma unroll
   for (int i = 0; i < MB; ++i) oacc[i] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;   // running max of raw scores, partial row sum
+  const float c = a.scale_log2;           // > 0
+  const float thr = 8.f / c;              // rescale only when the max grows by 2^8
 
-  const __bf16* kbase = a.k + (int64_t)kvh * a.k_hs;
-  const __bf16* vbase = a.v + (int64_t)kvh * a.v_hs;
-  u32x4 kreg[PERT], vreg[PERT];
-  auto tile_of = [&](int t) { return t < nP ? pidx[t] : fidx[t - nP]; };
-  auto gload = [&](int n) {
-#pragma unroll
-    for (int i = 0; i < PERT; ++i) {
-      const int idx = tid + NT * i, r = idx / NCH, c = idx % NCH;
-      const int key = n * BN_F + r;
-      if (key < a.Tk) {
-        kreg[i] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)key * a.k_ts + 8 * c);
-        vreg[i] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)key * a.v_ts + 8 * c);
-      } else {
-        kreg[i] = u32x4{0, 0, 0, 0};
-        vreg[i] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto lstore = [&](int stage) {
-    char* kt = smem + stage * 2 * TILE_B;
-    char* vt = kt + TILE_B;
-#pragma unroll
-    for (int i = 0; i < PERT; ++i) {
-      const int idx = tid + NT * i, r = idx / NCH, c = idx % NCH;
-      *reinterpret_cast<u32x4*>(kt + lds_off<D>(r, c)) = kreg[i];
-      *reinterpret_cast<u32x4*>(vt + lds_off<D>(r, c)) = vreg[i];
-    }
-  };
-
-  if (nT > 0) {
-    gload(tile_of(0));
-    lstore(0);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < nT; ++t) {
-    const int stage = t & 1;
+  auto tile = [&](auto stage_c, int t) {
+    constexpr int stage = decltype(stage_c)::value;
     const bool masked = t < nP;
     const int n = tile_of(t);
-    if (t + 1 < nT) gload(tile_of(t + 1));
-    const char* kt = smem + stage * 2 * TILE_B;
-    const char* vt = kt + TILE_B;
+    if (t + 1 < nT) issue(t + 1, stage ^ 1);
+    const __attribute__((address_space(3))) char* lb =
+        (const __attribute__((address_space(3))) char*)smem + stage * STAGE_B;
 
-    // S^T = K Q^T: rows = keys 32kb + (8(r/4) + 4*h32 + r%4), column = this lane's query
+    // S^T = K Q^T; two independent accumulation chains interleaved
     f32x16 sacc[KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      sacc[kb] = f32x16{};
+    for (int kb = 0; kb < KB; ++kb) sacc[kb] = f32x16{};
 #pragma unroll
-      for (int k = 0; k < KS; ++k) {
-        const bf16x8 kop = read_row_operand<D>(kt, 32 * kb + l32, 2 * k + h32);
+    for (int k = 0; k < KS; ++k)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        u32x4 u = *(const __attribute__((address_space(3))) u32x4*)(lb + kaddr[k] + kb * 32 * D * 2);
+        bf16x8 kop;
+        __builtin_memcpy(&kop, &u, 16);
         sacc[kb] = mfma32(kop, qop[k], sacc[kb]);
       }
-    }
-
-    float x[KB][16];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[kb][r] = sacc[kb][r] * a.scale_log2;
 
     if (masked) {
-      // valid keys of this row inside [n0, n0 + BN_F) as a bit mask
       const int n0 = n * BN_F;
       uint64_t mk = 0;
       for (int si = 0; si < nS; ++si) {
-        const Slice s = load_slice(mv.slices, sidx[si]);
+        const Slice sl = load_slice(mv.slices, sidx[si]);
         int lo, hi;
-        row_interval(s, qrow, lo, hi);
+        row_interval(sl, qrow, lo, hi);
         lo = max(lo, n0);
         hi = min(hi, n0 + BN_F - 1);
         if (lo <= hi) mk |= bit_range(lo - n0, hi - n0);
@@ -147,7 +140,7 @@ __global__ __launch_bounds__(NT, 2) void ffa_fwd_kernel(FwdArgs a) {
         const uint32_t w = static_cast<uint32_t>(mk >> (32 * kb));
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (!((w >> (8 * (r >> 2) + (r & 3))) & 1u)) x[kb][r] = -INFINITY;
+          if (!((w >> (8 * (r >> 2) + (r & 3))) & 1u)) sacc[kb][r] = -INFINITY;
       }
     }
 
@@ -155,45 +148,61 @@ __global__ __launch_bounds__(NT, 2) void ffa_fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, x[kb][r]);
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
     mx = wave_swap_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    if (__ballot(mx > m_run + thr) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
+      l_run *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[mb][r] *= alpha;
+      m_run = m_new;
+    }
+    const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
     float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float pv = __builtin_amdgcn_exp2f(x[kb][r] - m_use);
-        x[kb][r] = pv;
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], c, -mc));
+        sacc[kb][r] = pv;
         psum += pv;
       }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[mb][r] *= alpha;
+    l_run += psum;
 
     // O^T += V^T P^T over 16-key chunks
 #pragma unroll
-    for (int c = 0; c < BN_F / 16; ++c) {
-      const int kb = c >> 1, c2 = c & 1;
-      const bf16x8 pop = pack_bf16x8(&x[kb][8 * c2]);
+    for (int cc = 0; cc < BN_F / 16; ++cc) {
+      const int kb = cc >> 1, c2 = cc & 1;
+      bf16x8 pop;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pop[e] = static_cast<__bf16>(sacc[kb][8 * c2 + e]);
+      const int roff = TILE_B + (32 * kb + 16 * c2) * D * 2;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        const bf16x8 vop = read_tr_operand<D>(vt, 32 * kb + 16 * c2 + 4 * h32,
-                                              32 * mb + 16 * (g16 & 1), t16);
+        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4_t*)(lb + vaddr[mb][0] + roff));
+        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4_t*)(lb + vaddr[mb][1] + roff));
+        const i16x8 vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        bf16x8 vop;
+        __builtin_memcpy(&vop, &vv, 16);
         oacc[mb] = mfma32(vop, pop, oacc[mb]);
       }
     }
-
-    if (t + 1 < nT) lstore(stage ^ 1);
     __syncthreads();
+  };
+
+  if (nT > 0) issue(0, 0);
+  __syncthreads();
+  for (int t = 0; t < nT; t += 2) {
+    tile(std::integral_constant<int, 0>{}, t);
+    if (t + 1 < nT) tile(std::integral_constant<int, 1>{}, t + 1);
   }
 
-  // epilogue: O = O^T / l, LSE = m*ln2 + ln l (natural log, scale included)
+  // epilogue: O = O^T / l, LSE = m*scale + ln l (natural log)
   const float l_tot = wave_swap_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qok) {
@@ -208,7 +217,7 @@ __global__ __launch_bounds__(NT, 2) void ffa_fwd_kernel(FwdArgs a) {
         *reinterpret_cast<bf16x4*>(op + 32 * mb + 8 * j + 4 * h32) = w;
       }
     if (h32 == 0)
-      a.lse[(int64_t)head * a.Tq + qrow] = l_tot > 0.f ? m_run * LN2 + logf(l_tot) : -INFINITY;
+      a.lse[(int64_t)head * a.Tq + qrow] = l_tot > 0.f ? m_run * a.scale + logf(l_tot) : -INFINITY;
   }
 }
 

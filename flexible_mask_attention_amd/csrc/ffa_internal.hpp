@@ -176,6 +176,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
@@ -251,6 +252,56 @@ __device__ __forceinline__ bf16x8 read_row_operand(const char* tile, int r, int 
   __builtin_memcpy(&v, &u, 16);
   return v;
 }
+
+// Buffer resource over [base, base + num_bytes): loads past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {
+  // the arguments are wave-uniform; keep them in scalar registers so the
+  // descriptor is an SGPR quad (no per-lane waterfall around the loads)
+  const int n = __builtin_amdgcn_readfirstlane((int)num_bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
+}
+
+// 16 bytes per lane from global straight into LDS: lane l writes
+// lds_base + 16*l (lds_base must be wave-uniform).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds_base, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16,
+                                           (int)voff, 0, 0, 0);
+}
+
+// Per-lane byte offsets for loading a [ROWS][D] bf16 tile whose rows are
+// `ts_bytes` apart in global memory into the swizzled LDS layout with 16-byte
+// direct loads.  Wave w fills rows [ROWS/4*w, ROWS/4*(w+1)); its i-th load
+// covers 1024 contiguous LDS bytes, i.e. rows_per_load = 1024 / (2D) whole
+// rows, and lane l lands on chunk position l % (D/8) of row l / (D/8), which
+// holds logical chunk position ^ swz(row).
+template <int D, int ROWS>
+struct TileDma {
+  static constexpr int ROWB = D * 2;
+  static constexpr int CPR = D / 8;              // chunks per row
+  static constexpr int RPL = 1024 / ROWB;        // rows per load
+  static constexpr int NL = ROWS / 4 / RPL;      // loads per wave
+  uint32_t voff[NL];
+  int row0;                                       // first row of this wave
+  __device__ __forceinline__ void init(int wid, int lane, int64_t ts_elems) {
+    row0 = wid * (ROWS / 4);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int r = row0 + i * RPL + lane / CPR;
+      const int c = (lane % CPR) ^ swz<D>(r);
+      voff[i] = (uint32_t)(r * ts_elems * 2 + c * 16);
+    }
+  }
+  // rows [row_base, row_base + ROWS) of a tensor (base pointer of row 0 of the
+  // head), valid_rows of them in bounds
+  __device__ __forceinline__ void load(const __bf16* head_base, int64_t ts_elems, int row_base,
+                                       int valid_rows, char* lds_tile) const {
+    const __bf16* b = head_base + (int64_t)row_base * ts_elems;
+    const int vr = valid_rows < 0 ? 0 : (valid_rows > ROWS ? ROWS : valid_rows);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(b, (uint32_t)(vr * ts_elems * 2));
+#pragma unroll
+    for (int i = 0; i < NL; ++i) dma16(r, lds_tile + (row0 + i * RPL) * ROWB, voff[i]);
+  }
+};
 
 __device__ __forceinline__ float wave_swap_max(float x) {
   auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -80,7 +80,8 @@ typedef enum {
 
 typedef struct {
   const void* ptr;       /* device, 16-byte aligned */
-  int64_t token_stride;  /* elements between consecutive tokens (multiple of 8) */
+  int64_t token_stride;  /* elements between consecutive tokens: multiple of 8,
+                            >= head_dim and < 2^23 when there is more than one token */
   int64_t head_stride;   /* elements between consecutive heads (multiple of 8) */
 } ffa_tensor_in;
 
@@ -96,7 +97,7 @@ typedef struct {
   int32_t num_heads_q;   /* >= 1, multiple of num_heads_kv */
   int32_t num_heads_kv;  /* >= 1 */
   int32_t head_dim;      /* 64 or 128 */
-  float softmax_scale;   /* finite, non-zero; 1/sqrt(head_dim) is the usual choice */
+  float softmax_scale;   /* finite, > 0; 1/sqrt(head_dim) is the usual choice */
 } ffa_shape;
 
 /* Host-side summary of a block-metadata buffer (pure pointer arithmetic; no

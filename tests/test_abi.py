@@ -58,6 +58,9 @@ def test_host_validation_returns_before_enqueue():
     # non-finite / zero scale
     assert L.ffa_fwd(P(_shape(scale=float("nan"))), good, good, good, meta, goodo, lse, None) == 1
     assert L.ffa_fwd(P(_shape(scale=0.0)), good, good, good, meta, goodo, lse, None) == 1
+    assert L.ffa_fwd(P(_shape(scale=-0.5)), good, good, good, meta, goodo, lse, None) == 1
+    # token stride below head_dim
+    assert L.ffa_fwd(P(_shape()), ffa.TensorIn(0x1000, 32, 64), good, good, meta, goodo, lse, None) == 1
     # null / misaligned tensor pointers, bad strides
     assert L.ffa_fwd(P(_shape()), ffa.TensorIn(0, 128, 64), good, good, meta, goodo, lse, None) == 1
     assert L.ffa_fwd(P(_shape()), ffa.TensorIn(0x1002, 128, 64), good, good, meta, goodo, lse, None) == 1
