@@ -172,7 +172,7 @@ FFA_API ffa_status ffa_bwd_workspace_size(const ffa_shape* shape, size_t* bytes)
   ffa_status st = check_shape(shape);
   if (st != FFA_OK) return st;
   if (!bytes) return FFA_ERR_INVALID_ARGUMENT;
-  *bytes = (size_t)align256(4LL * shape->num_heads_q * shape->seqlen_q);
+  *bytes = (size_t)(2 * align256(4LL * shape->num_heads_q * shape->seqlen_q));
   return FFA_OK;
 }
 
@@ -220,6 +220,8 @@ FFA_API ffa_status ffa_bwd_phases(const ffa_shape* shape, ffa_tensor_in q, ffa_t
   a.dout = static_cast<const __bf16*>(dout.ptr);
   a.lse = lse;
   a.dvec = static_cast<float*>(d_ws);
+  a.lvec = reinterpret_cast<float*>(static_cast<char*>(d_ws) +
+                                    align256(4LL * shape->num_heads_q * shape->seqlen_q));
   a.dq = static_cast<__bf16*>(dq.ptr);
   a.dk = static_cast<__bf16*>(dk.ptr);
   a.dv = static_cast<__bf16*>(dv.ptr);

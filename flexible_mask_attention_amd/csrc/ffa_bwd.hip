@@ -19,6 +19,8 @@
 // lanes), so P and dS feed the dV^T / dK^T MFMAs as B operands and dO^T, Q^T
 // come from LDS through transposed reads.  dq mirrors the forward (lanes own
 // query rows).
+#include <type_traits>
+
 #include "ffa_internal.hpp"
 
 namespace ffa {
@@ -50,7 +52,11 @@ __global__ __launch_bounds__(NT) void ffa_bwd_pre_kernel(BwdArgs a) {
   }
 #pragma unroll
   for (int off = G / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, G);
-  if (ok && part == 0) a.dvec[(int64_t)h * a.Tq + i] = acc;
+  if (ok && part == 0) {
+    a.dvec[(int64_t)h * a.Tq + i] = acc;
+    const float l = a.lse[(int64_t)h * a.Tq + i];
+    a.lvec[(int64_t)h * a.Tq + i] = (l == -INFINITY) ? 0.f : l * LOG2E;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -61,8 +67,6 @@ __global__ __launch_bounds__(NT, 1) void ffa_bwd_dkdv_kernel(BwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int TILE_B = BM_B * D * 2;          // bytes of one Q or dO tile
   constexpr int STAGE_B = 2 * TILE_B + 2 * BM_B * 4;
-  constexpr int NCH = D / 8;
-  constexpr int PERT = BM_B * NCH / NT;
   constexpr int QB = BM_B / 32;                 // 32-row query blocks per tile
   constexpr int MB = D / 32;
   constexpr int KS = D / 16;
@@ -71,7 +75,8 @@ __global__ __launch_bounds__(NT, 1) void ffa_bwd_dkdv_kernel(BwdArgs a) {
   const MetaHeader* hd = mv.hdr;
   if (hd->status != 0 || hd->seqlen_q != a.Tq || hd->seqlen_k != a.Tk) return;
 
-  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h32 = lane >> 5, t16 = lane & 15, g16 = lane >> 4;
   const int kvh = blockIdx.x % a.Hkv;
   const int n = mv.sched_b[blockIdx.x / a.Hkv];
@@ -99,6 +104,25 @@ __global__ __launch_bounds__(NT, 1) void ffa_bwd_dkdv_kernel(BwdArgs a) {
     }
   }
 
+  // loop-invariant LDS addresses
+  int raddr[KS];                 // 128-bit row reads (row l32, chunk 2k + h32)
+#pragma unroll
+  for (int k = 0; k < KS; ++k) raddr[k] = lds_off<D>(l32, 2 * k + h32);
+  int taddr[MB][2];              // transposed reads (rows 4*h32 + t/4 (+8), cols 32mb + ...)
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int rr = 4 * h32 + (t16 >> 2) + 8 * j;
+      const int cc = 32 * mb + 16 * (g16 & 1) + 4 * (t16 & 3);
+      taddr[mb][j] = lds_off<D>(rr, cc >> 3) + ((cc & 7) << 1);
+    }
+  const int laddr = 2 * TILE_B + 16 * h32;   // row-stat reads: + (32qb + 8j) * 4
+
+  TileDma<D, BM_B> dq_dma, dg_dma;
+  dq_dma.init(wid, lane, a.q_ts);
+  dg_dma.init(wid, lane, a.do_ts);
+
   f32x16 dkacc[MB], dvacc[MB];
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
@@ -106,71 +130,34 @@ __global__ __launch_bounds__(NT, 1) void ffa_bwd_dkdv_kernel(BwdArgs a) {
     dvacc[i] = f32x16{};
   }
 
-  u32x4 qreg[PERT], dreg[PERT];
-  float lreg = 0.f;   // threads 0..BM_B-1: lse*log2e of one row, BM_B..2BM_B-1: D of one row
   const int total = G * nT;
   auto tile_of = [&](int t) { return t < nP ? pidx[t] : fidx[t - nP]; };
-  auto gload = [&](int u) {
+  auto issue = [&](int u, int stage) {
     const int hq = kvh * G + u / nT;
     const int m = tile_of(u % nT);
-    const __bf16* qb = a.q + (int64_t)hq * a.q_hs;
-    const __bf16* gb = a.dout + (int64_t)hq * a.do_hs;
-#pragma unroll
-    for (int i = 0; i < PERT; ++i) {
-      const int idx = tid + NT * i, r = idx / NCH, c = idx % NCH;
-      const int row = m * BM_B + r;
-      if (row < a.Tq) {
-        qreg[i] = *reinterpret_cast<const u32x4*>(qb + (int64_t)row * a.q_ts + 8 * c);
-        dreg[i] = *reinterpret_cast<const u32x4*>(gb + (int64_t)row * a.do_ts + 8 * c);
-      } else {
-        qreg[i] = u32x4{0, 0, 0, 0};
-        dreg[i] = u32x4{0, 0, 0, 0};
-      }
-    }
-    if (tid < 2 * BM_B) {
-      const int row = m * BM_B + (tid % BM_B);
-      float x = 0.f;
-      if (row < a.Tq) {
-        if (tid < BM_B) {
-          const float l = a.lse[(int64_t)hq * a.Tq + row];
-          x = (l == -INFINITY) ? 0.f : l * LOG2E;
-        } else {
-          x = a.dvec[(int64_t)hq * a.Tq + row];
-        }
-      }
-      lreg = x;
+    char* st = smem + stage * STAGE_B;
+    const int vr = a.Tq - m * BM_B;
+    dq_dma.load(a.q + (int64_t)hq * a.q_hs, a.q_ts, m * BM_B, vr, st);
+    dg_dma.load(a.dout + (int64_t)hq * a.do_hs, a.do_ts, m * BM_B, vr, st + TILE_B);
+    if (wid < 2) {
+      const float* src = (wid == 0 ? a.lvec : a.dvec) + (int64_t)hq * a.Tq + m * BM_B;
+      const int rows = vr < 0 ? 0 : (vr > BM_B ? BM_B : vr);
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(src, (uint32_t)(rows * 4));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(st + 2 * TILE_B + wid * BM_B * 4), 4,
+          lane * 4, 0, 0, 0);
     }
   };
-  auto lstore = [&](int stage) {
-    char* qt = smem + stage * STAGE_B;
-    char* gt = qt + TILE_B;
-    float* lt = reinterpret_cast<float*>(gt + TILE_B);
-#pragma unroll
-    for (int i = 0; i < PERT; ++i) {
-      const int idx = tid + NT * i, r = idx / NCH, c = idx % NCH;
-      *reinterpret_cast<u32x4*>(qt + lds_off<D>(r, c)) = qreg[i];
-      *reinterpret_cast<u32x4*>(gt + lds_off<D>(r, c)) = dreg[i];
-    }
-    if (tid < 2 * BM_B) lt[tid] = lreg;
-  };
+  const float c = a.scale_log2;
 
-  if (total > 0) {
-    gload(0);
-    lstore(0);
-  }
-  __syncthreads();
-
-  for (int u = 0; u < total; ++u) {
-    const int stage = u & 1;
+  auto tile = [&](auto stage_c, int u) {
+    constexpr int stage = decltype(stage_c)::value;
     const int t = u % nT;
     const bool masked = t < nP;
     const int m = tile_of(t);
-    const int hq = kvh * G + u / nT;
-    (void)hq;
-    if (u + 1 < total) gload(u + 1);
-    const char* qt = smem + stage * STAGE_B;
-    const char* gt = qt + TILE_B;
-    const float* lt = reinterpret_cast<const float*>(gt + TILE_B);
+    if (u + 1 < total) issue(u + 1, stage ^ 1);
+    const __attribute__((address_space(3))) char* lb =
+        (const __attribute__((address_space(3))) char*)smem + stage * STAGE_B;
 
     // S = Q K^T and dP = dO V^T; lane = key, registers = rows 32qb + 8(r/4) + 4*h32 + r%4
     f32x16 sacc[QB], pacc[QB];
@@ -178,14 +165,19 @@ __global__ __launch_bounds__(NT, 1) void ffa_bwd_dkdv_kernel(BwdArgs a) {
     for (int qb = 0; qb < QB; ++qb) {
       sacc[qb] = f32x16{};
       pacc[qb] = f32x16{};
+    }
 #pragma unroll
-      for (int k = 0; k < KS; ++k) {
-        const bf16x8 qa = read_row_operand<D>(qt, 32 * qb + l32, 2 * k + h32);
+    for (int k = 0; k < KS; ++k)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        bf16x8 qa, ga;
+        u32x4 u1 = *(const __attribute__((address_space(3))) u32x4*)(lb + raddr[k] + qb * 32 * D * 2);
+        u32x4 u2 = *(const __attribute__((address_space(3))) u32x4*)(lb + TILE_B + raddr[k] + qb * 32 * D * 2);
+        __builtin_memcpy(&qa, &u1, 16);
+        __builtin_memcpy(&ga, &u2, 16);
         sacc[qb] = mfma32(qa, kop[k], sacc[qb]);
-        const bf16x8 ga = read_row_operand<D>(gt, 32 * qb + l32, 2 * k + h32);
         pacc[qb] = mfma32(ga, vop[k], pacc[qb]);
       }
-    }
 
     uint64_t mk = ~0ull;
     if (masked) {
@@ -197,9 +189,9 @@ __global__ __launch_bounds__(NT, 1) void ffa_bwd_dkdv_kernel(BwdArgs a) {
       const int32_t* sidx = mv.var + hd->list_off[L_QS] + s0;
       mk = 0;
       for (int si = 0; si < nS; ++si) {
-        const Slice s = load_slice(mv.slices, sidx[si]);
+        const Slice sl = load_slice(mv.slices, sidx[si]);
         int lo, hi;
-        col_interval(s, key, lo, hi);
+        col_interval(sl, key, lo, hi);
         lo = max(lo, m0);
         hi = min(hi, m0 + BM_B - 1);
         if (lo <= hi) mk |= bit_range(lo - m0, hi - m0);
@@ -207,44 +199,59 @@ __global__ __launch_bounds__(NT, 1) void ffa_bwd_dkdv_kernel(BwdArgs a) {
       mk >>= 4 * h32;
     }
 
-    float p[QB][16], ds[QB][16];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const uint32_t w = static_cast<uint32_t>(mk >> (32 * qb));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int row = 32 * qb + 8 * j + 4 * h32;
-        const f32x4 lse4 = *reinterpret_cast<const f32x4*>(lt + row);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(lt + BM_B + row);
+        const int ro = laddr + (32 * qb + 8 * j) * 4;
+        const f32x4 l4 = *(const __attribute__((address_space(3))) f32x4*)(lb + ro);
+        const f32x4 d4 = *(const __attribute__((address_space(3))) f32x4*)(lb + ro + BM_B * 4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 4 * j + i;
-          float pv = __builtin_amdgcn_exp2f(sacc[qb][r] * a.scale_log2 - lse4[i]);
+          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][r], c, -l4[i]));
           if (masked && !((w >> (8 * j + i)) & 1u)) pv = 0.f;
-          p[qb][r] = pv;
-          ds[qb][r] = pv * (pacc[qb][r] - d4[i]);
+          sacc[qb][r] = pv;
+          pacc[qb][r] = pv * (pacc[qb][r] - d4[i]);
         }
       }
     }
 
     // dV^T += dO^T P and dK^T += Q^T dS over 16-row chunks
 #pragma unroll
-    for (int c = 0; c < BM_B / 16; ++c) {
-      const int qb = c >> 1, c2 = c & 1;
-      const bf16x8 pb = pack_bf16x8(&p[qb][8 * c2]);
-      const bf16x8 sb = pack_bf16x8(&ds[qb][8 * c2]);
+    for (int cc = 0; cc < BM_B / 16; ++cc) {
+      const int qb = cc >> 1, c2 = cc & 1;
+      bf16x8 pb, sb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pb[e] = static_cast<__bf16>(sacc[qb][8 * c2 + e]);
+        sb[e] = static_cast<__bf16>(pacc[qb][8 * c2 + e]);
+      }
+      const int roff = (32 * qb + 16 * c2) * D * 2;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        const int r0 = 32 * qb + 16 * c2 + 4 * h32, cb = 32 * mb + 16 * (g16 & 1);
-        const bf16x8 ga = read_tr_operand<D>(gt, r0, cb, t16);
+        const i16x4 g0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lb + TILE_B + taddr[mb][0] + roff));
+        const i16x4 g1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lb + TILE_B + taddr[mb][1] + roff));
+        const i16x4 q0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lb + taddr[mb][0] + roff));
+        const i16x4 q1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lb + taddr[mb][1] + roff));
+        const i16x8 gg = __builtin_shufflevector(g0, g1, 0, 1, 2, 3, 4, 5, 6, 7);
+        const i16x8 qq = __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7);
+        bf16x8 ga, qa;
+        __builtin_memcpy(&ga, &gg, 16);
+        __builtin_memcpy(&qa, &qq, 16);
         dvacc[mb] = mfma32(ga, pb, dvacc[mb]);
-        const bf16x8 qa = read_tr_operand<D>(qt, r0, cb, t16);
         dkacc[mb] = mfma32(qa, sb, dkacc[mb]);
       }
     }
-
-    if (u + 1 < total) lstore(stage ^ 1);
     __syncthreads();
+  };
+
+  if (total > 0) issue(0, 0);
+  __syncthreads();
+  for (int u = 0; u < total; u += 2) {
+    tile(std::integral_constant<int, 0>{}, u);
+    if (u + 1 < total) tile(std::integral_constant<int, 1>{}, u + 1);
   }
 
   if (kok) {
@@ -273,8 +280,7 @@ template <int D>
 __global__ __launch_bounds__(NT, 1) void ffa_bwd_dq_kernel(BwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int TILE_B = BN_F * D * 2;
-  constexpr int NCH = D / 8;
-  constexpr int PERT = BN_F * NCH / NT;
+  constexpr int STAGE_B = 2 * TILE_B;
   constexpr int KB = BN_F / 32;
   constexpr int MB = D / 32;
   constexpr int KS = D / 16;
@@ -283,7 +289,8 @@ __global__ __launch_bounds__(NT, 1) void ffa_bwd_dq_kernel(BwdArgs a) {
   const MetaHeader* hd = mv.hdr;
   if (hd->status != 0 || hd->seqlen_q != a.Tq || hd->seqlen_k != a.Tk) return;
 
-  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h32 = lane >> 5, t16 = lane & 15, g16 = lane >> 4;
   const int head = blockIdx.x % a.Hq;
   const int m = mv.sched_f[blockIdx.x / a.Hq];
@@ -311,82 +318,78 @@ __global__ __launch_bounds__(NT, 1) void ffa_bwd_dq_kernel(BwdArgs a) {
       __builtin_memcpy(&gop[k], &w, 16);
     }
   }
-  float lse_l2 = 0.f, dval = 0.f;
+  float l2 = 0.f, dval = 0.f;
   if (qok) {
-    const float l = a.lse[(int64_t)head * a.Tq + qrow];
-    lse_l2 = (l == -INFINITY) ? 0.f : l * LOG2E;
+    l2 = a.lvec[(int64_t)head * a.Tq + qrow];
     dval = a.dvec[(int64_t)head * a.Tq + qrow];
   }
+
+  int raddr[KS];
+#pragma unroll
+  for (int k = 0; k < KS; ++k) raddr[k] = lds_off<D>(l32, 2 * k + h32);
+  int taddr[MB][2];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int rr = 4 * h32 + (t16 >> 2) + 8 * j;
+      const int cc = 32 * mb + 16 * (g16 & 1) + 4 * (t16 & 3);
+      taddr[mb][j] = lds_off<D>(rr, cc >> 3) + ((cc & 7) << 1);
+    }
+
+  TileDma<D, BN_F> dmk, dmv;
+  dmk.init(wid, lane, a.k_ts);
+  dmv.init(wid, lane, a.v_ts);
+  const __bf16* kbase = a.k + (int64_t)kvh * a.k_hs;
+  const __bf16* vbase = a.v + (int64_t)kvh * a.v_hs;
+  auto tile_of = [&](int t) { return t < nP ? pidx[t] : fidx[t - nP]; };
+  auto issue = [&](int t, int stage) {
+    const int n = tile_of(t);
+    char* st = smem + stage * STAGE_B;
+    dmk.load(kbase, a.k_ts, n * BN_F, a.Tk - n * BN_F, st);
+    dmv.load(vbase, a.v_ts, n * BN_F, a.Tk - n * BN_F, st + TILE_B);
+  };
 
   f32x16 dqacc[MB];
 #pragma unroll
   for (int i = 0; i < MB; ++i) dqacc[i] = f32x16{};
+  const float c = a.scale_log2;
 
-  const __bf16* kbase = a.k + (int64_t)kvh * a.k_hs;
-  const __bf16* vbase = a.v + (int64_t)kvh * a.v_hs;
-  u32x4 kreg[PERT], vreg[PERT];
-  auto tile_of = [&](int t) { return t < nP ? pidx[t] : fidx[t - nP]; };
-  auto gload = [&](int n) {
-#pragma unroll
-    for (int i = 0; i < PERT; ++i) {
-      const int idx = tid + NT * i, r = idx / NCH, c = idx % NCH;
-      const int key = n * BN_F + r;
-      if (key < a.Tk) {
-        kreg[i] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)key * a.k_ts + 8 * c);
-        vreg[i] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)key * a.v_ts + 8 * c);
-      } else {
-        kreg[i] = u32x4{0, 0, 0, 0};
-        vreg[i] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto lstore = [&](int stage) {
-    char* kt = smem + stage * 2 * TILE_B;
-    char* vt = kt + TILE_B;
-#pragma unroll
-    for (int i = 0; i < PERT; ++i) {
-      const int idx = tid + NT * i, r = idx / NCH, c = idx % NCH;
-      *reinterpret_cast<u32x4*>(kt + lds_off<D>(r, c)) = kreg[i];
-      *reinterpret_cast<u32x4*>(vt + lds_off<D>(r, c)) = vreg[i];
-    }
-  };
-
-  if (nT > 0) {
-    gload(tile_of(0));
-    lstore(0);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < nT; ++t) {
-    const int stage = t & 1;
+  auto tile = [&](auto stage_c, int t) {
+    constexpr int stage = decltype(stage_c)::value;
     const bool masked = t < nP;
     const int n = tile_of(t);
-    if (t + 1 < nT) gload(tile_of(t + 1));
-    const char* kt = smem + stage * 2 * TILE_B;
-    const char* vt = kt + TILE_B;
+    if (t + 1 < nT) issue(t + 1, stage ^ 1);
+    const __attribute__((address_space(3))) char* lb =
+        (const __attribute__((address_space(3))) char*)smem + stage * STAGE_B;
 
     f32x16 sacc[KB], pacc[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       sacc[kb] = f32x16{};
       pacc[kb] = f32x16{};
+    }
 #pragma unroll
-      for (int k = 0; k < KS; ++k) {
-        const bf16x8 ka = read_row_operand<D>(kt, 32 * kb + l32, 2 * k + h32);
+    for (int k = 0; k < KS; ++k)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        bf16x8 ka, va;
+        u32x4 u1 = *(const __attribute__((address_space(3))) u32x4*)(lb + raddr[k] + kb * 32 * D * 2);
+        u32x4 u2 = *(const __attribute__((address_space(3))) u32x4*)(lb + TILE_B + raddr[k] + kb * 32 * D * 2);
+        __builtin_memcpy(&ka, &u1, 16);
+        __builtin_memcpy(&va, &u2, 16);
         sacc[kb] = mfma32(ka, qop[k], sacc[kb]);
-        const bf16x8 va = read_row_operand<D>(vt, 32 * kb + l32, 2 * k + h32);
         pacc[kb] = mfma32(va, gop[k], pacc[kb]);
       }
-    }
 
     uint64_t mk = ~0ull;
     if (masked) {
       const int n0 = n * BN_F;
       mk = 0;
       for (int si = 0; si < nS; ++si) {
-        const Slice s = load_slice(mv.slices, sidx[si]);
+        const Slice sl = load_slice(mv.slices, sidx[si]);
         int lo, hi;
-        row_interval(s, qrow, lo, hi);
+        row_interval(sl, qrow, lo, hi);
         lo = max(lo, n0);
         hi = min(hi, n0 + BN_F - 1);
         if (lo <= hi) mk |= bit_range(lo - n0, hi - n0);
@@ -394,32 +397,42 @@ __global__ __launch_bounds__(NT, 1) void ffa_bwd_dq_kernel(BwdArgs a) {
       mk >>= 4 * h32;
     }
 
-    float ds[KB][16];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const uint32_t w = static_cast<uint32_t>(mk >> (32 * kb));
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pv = __builtin_amdgcn_exp2f(sacc[kb][r] * a.scale_log2 - lse_l2);
+        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], c, -l2));
         if (masked && !((w >> (8 * (r >> 2) + (r & 3))) & 1u)) pv = 0.f;
-        ds[kb][r] = pv * (pacc[kb][r] - dval);
+        pacc[kb][r] = pv * (pacc[kb][r] - dval);
       }
     }
 
 #pragma unroll
-    for (int c = 0; c < BN_F / 16; ++c) {
-      const int kb = c >> 1, c2 = c & 1;
-      const bf16x8 sb = pack_bf16x8(&ds[kb][8 * c2]);
+    for (int cc = 0; cc < BN_F / 16; ++cc) {
+      const int kb = cc >> 1, c2 = cc & 1;
+      bf16x8 sb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sb[e] = static_cast<__bf16>(pacc[kb][8 * c2 + e]);
+      const int roff = (32 * kb + 16 * c2) * D * 2;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        const bf16x8 ka = read_tr_operand<D>(kt, 32 * kb + 16 * c2 + 4 * h32,
-                                             32 * mb + 16 * (g16 & 1), t16);
+        const i16x4 k0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lb + taddr[mb][0] + roff));
+        const i16x4 k1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lb + taddr[mb][1] + roff));
+        const i16x8 kk = __builtin_shufflevector(k0, k1, 0, 1, 2, 3, 4, 5, 6, 7);
+        bf16x8 ka;
+        __builtin_memcpy(&ka, &kk, 16);
         dqacc[mb] = mfma32(ka, sb, dqacc[mb]);
       }
     }
-
-    if (t + 1 < nT) lstore(stage ^ 1);
     __syncthreads();
+  };
+
+  if (nT > 0) issue(0, 0);
+  __syncthreads();
+  for (int t = 0; t < nT; t += 2) {
+    tile(std::integral_constant<int, 0>{}, t);
+    if (t + 1 < nT) tile(std::integral_constant<int, 1>{}, t + 1);
   }
 
   if (qok) {

@@ -71,7 +71,7 @@ def test_host_validation_returns_before_enqueue():
     assert L.ffa_fwd(None, good, good, good, meta, goodo, lse, None) == 1
     # backward workspace too small / null
     ws = ctypes.c_size_t()
-    assert L.ffa_bwd_workspace_size(P(_shape()), P(ws)) == 0 and ws.value == 2 * 256 * 4
+    assert L.ffa_bwd_workspace_size(P(_shape()), P(ws)) == 0 and ws.value == 2 * (2 * 256 * 4)
     assert L.ffa_bwd(P(_shape()), good, good, good, good, lse, good, meta, goodo, goodo, goodo,
                      0x100000, ws.value - 1, None) == 3
     assert L.ffa_bwd(P(_shape()), good, good, good, good, lse, good, meta, goodo, goodo, goodo,
