@@ -25,7 +25,8 @@ Readings where the pages are silent (each listed in the design notes):
   out-of-bounds rule with the axes swapped; CSR lists ascending, Full and
   Partial kept apart.
 
-Everything is float64 (bf16 inputs upcast exactly).  The forward is two-pass
+Everything is float64 (bf16 inputs upcast exactly), written with numpy and plain
+PyTorch CPU ops (library matmul, exp, log).  The forward is two-pass
 (LSE first, then O), unlike the GPU's online softmax.
 """
 from __future__ import annotations
@@ -40,15 +41,6 @@ FULL, CAUSAL, INV_CAUSAL, BI_CAUSAL = 0, 1, 2, 3
 # status flags for a slice table (bitwise OR, same meaning as the library's
 # device status word)
 ERR_BOUNDS, ERR_TYPE, ERR_OVERLAP = 1, 2, 4
-
-
-def _as_f64(x) -> np.ndarray:
-    """torch tensor (any float dtype, CPU) or ndarray -> float64 ndarray (exact upcast)."""
-    if hasattr(x, "detach"):
-        x = x.detach().to("cpu")
-        import torch  # local: the oracle itself needs torch only to read tensors
-        return x.to(torch.float64).numpy()
-    return np.asarray(x, dtype=np.float64)
 
 
 # ---------------------------------------------------------------------------
@@ -142,6 +134,17 @@ def row_intervals_vec(s, rows: np.ndarray):
     hi = np.minimum(Lk - 1, r + Lk - Lq) if t in (CAUSAL, BI_CAUSAL) else np.full_like(r, Lk - 1)
     ok = (rows >= q0) & (rows < q1) & (lo <= hi) & (Lk > 0)
     return k0 + lo, k0 + hi, ok
+
+
+def col_intervals_vec(s, cols: np.ndarray):
+    """Vectorised ``col_interval`` over an int array of keys: (lo, hi, ok)."""
+    q0, q1, k0, k1, t = s
+    cols = np.asarray(cols, dtype=np.int64)
+    c, Lq, Lk = cols - k0, q1 - q0, k1 - k0
+    lo = np.maximum(0, c - (Lk - Lq)) if t in (CAUSAL, BI_CAUSAL) else np.zeros_like(c)
+    hi = np.minimum(Lq - 1, c) if t in (INV_CAUSAL, BI_CAUSAL) else np.full_like(c, Lq - 1)
+    ok = (cols >= k0) & (cols < k1) & (lo <= hi) & (Lq > 0)
+    return q0 + lo, q0 + hi, ok
 
 
 def valid_keys(slices: Sequence, i: int) -> np.ndarray:
@@ -331,12 +334,14 @@ def block_meta(slices: Sequence, Tq: int, Tk: int, BM: int, BN: int, direction: 
 # c.4 / c.5  attention forward and backward
 # ---------------------------------------------------------------------------
 
-def _row_batches(rows: np.ndarray, slices: Sequence, max_elems: int):
+def _row_batches(rows: np.ndarray, slices: Sequence, max_elems: int, max_rows: int = 256):
     """Split sorted rows into batches; for each batch give the key window
     [w0, w1) that contains every valid key of every row in it and the (rows x
     window) validity mask built from the row intervals.  Rows are independent
     and keys outside the window are invalid for all rows of the batch, so
-    attention over the window equals attention over all keys."""
+    attention over the window equals attention over all keys.  A batch ends
+    after max_rows rows, when rows x window would pass max_elems, or where the
+    next row's keys do not touch the current window."""
     lo_all = np.full(len(rows), np.iinfo(np.int64).max, dtype=np.int64)
     hi_all = np.full(len(rows), -1, dtype=np.int64)
     ivs = []
@@ -352,148 +357,178 @@ def _row_batches(rows: np.ndarray, slices: Sequence, max_elems: int):
         b = a + 1
         w0 = lo_all[a] if hi_all[a] >= 0 else 0
         w1 = hi_all[a] + 1 if hi_all[a] >= 0 else 0
-        while b < n:
+        while b < n and b - a < max_rows:
             if hi_all[b] < 0:
                 nw0, nw1 = w0, w1
             elif w1 <= w0:
                 nw0, nw1 = lo_all[b], hi_all[b] + 1
             else:
+                if lo_all[b] > w1 or hi_all[b] + 1 < w0:
+                    break
                 nw0, nw1 = min(w0, lo_all[b]), max(w1, hi_all[b] + 1)
             if (b + 1 - a) * max(1, nw1 - nw0) > max_elems:
                 break
             w0, w1 = nw0, nw1
             b += 1
         w0, w1 = int(w0), int(max(w0, w1))
-        cols = np.arange(w0, w1)[None, :]
         mask = np.zeros((b - a, w1 - w0), dtype=bool)
         for lo, hi, ok in ivs:
-            sel = ok[a:b, None]
-            mask |= sel & (cols >= lo[a:b, None]) & (cols <= hi[a:b, None])
+            for r in np.nonzero(ok[a:b])[0]:
+                mask[r, lo[a + r] - w0:hi[a + r] + 1 - w0] = True
         yield a, b, w0, w1, mask
         a = b
 
 
-def _kv_head(h: int, Hq: int, Hkv: int) -> int:
-    return h // (Hq // Hkv)
+def _f64(x) -> "torch.Tensor":
+    """torch tensor / ndarray -> contiguous float64 CPU torch tensor (exact upcast)."""
+    import torch
+    if isinstance(x, np.ndarray):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64))
+    x = x.detach().to("cpu")
+    if x.dtype == torch.bfloat16:
+        x = x.to(torch.float32)
+    return x.to(torch.float64).contiguous()
+
+
+def _softmax_stats(S):
+    """Two-pass masked softmax over the last axis of S (masked entries are -inf):
+    pass 1 gives LSE = m + ln sum exp(S - m), pass 2 gives P = exp(S - LSE)
+    (formed as exp(S - m) / sum).  Rows without a valid entry get LSE = -inf
+    and P = 0."""
+    import torch
+    m = S.amax(dim=-1, keepdim=True)
+    m = torch.where(torch.isfinite(m), m, torch.zeros_like(m))
+    E = torch.exp(S - m)
+    z = E.sum(dim=-1, keepdim=True)
+    lse = m + torch.log(z)                                                    # pass 1
+    P = E.div_(torch.where(z > 0, z, torch.ones_like(z)))                     # pass 2
+    return lse, P
+
+
+def _attend(Qb, Kg, Vg, mask, scale):
+    """One row batch of one kv-head group: Qb [B, G, d], Kg/Vg [W, d] (the
+    batch's key window), mask [B, W] bool.  Returns S-derived (lse, P) and O."""
+    B, G, d = Qb.shape
+    S = scale * (Qb.reshape(B * G, d) @ Kg.T).view(B, G, -1)
+    S.masked_fill_(~mask[:, None, :], -math.inf)
+    lse, P = _softmax_stats(S)
+    O = (P.reshape(B * G, -1) @ Vg).view(B, G, d)
+    return lse[..., 0], P, O
 
 
 def forward(q, k, v, slices: Sequence, scale: float = None, rows=None,
-            max_elems: int = 1 << 22):
+            max_elems: int = 1 << 25):
     """O and LSE for the given query rows (default: all).
 
     For each head h and row i with valid key set J_i:
       s_ij = scale * q_i . k_j;  LSE_i = ln sum_{j in J_i} exp(s_ij)  (via max);
       O_i = sum_{j in J_i} exp(s_ij - LSE_i) v_j;
       J_i empty -> O_i = 0, LSE_i = -inf.
-    Returns O [len(rows), Hq, d] and LSE [Hq, len(rows)] (float64)."""
-    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    Query head h uses kv head h // (Hq / Hkv).
+    Returns O [len(rows), Hq, d] and LSE [Hq, len(rows)] (float64 ndarrays)."""
+    import torch
     Tq, Hq, d = q.shape
     Hkv = k.shape[1]
+    G = Hq // Hkv
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     rows = np.arange(Tq) if rows is None else np.asarray(rows, dtype=np.int64)
-    O = np.zeros((len(rows), Hq, d))
-    L = np.full((Hq, len(rows)), -np.inf)
-    with np.errstate(divide="ignore", invalid="ignore"):
-        _forward_batches(q, k, v, slices, scale, rows, max_elems, O, L)
-    return O, L
+    rows_t = torch.from_numpy(rows)
+    batches = list(_row_batches(rows, slices, max(1, max_elems // G)))
+    O = torch.zeros(len(rows), Hq, d, dtype=torch.float64)
+    L = torch.full((Hq, len(rows)), -math.inf, dtype=torch.float64)
+    for g in range(Hkv):
+        hs = slice(g * G, (g + 1) * G)
+        for a, b, w0, w1, mask in batches:
+            if w1 <= w0:
+                continue
+            Qb = _f64(q[rows_t[a:b], hs, :])
+            Kw, Vw = _f64(k[w0:w1, g, :]), _f64(v[w0:w1, g, :])
+            lse, _, Ob = _attend(Qb, Kw, Vw, torch.from_numpy(mask), scale)
+            O[a:b, hs, :] = Ob
+            L[hs, a:b] = lse.T
+    return O.numpy(), L.numpy()
 
 
-def _forward_batches(q, k, v, slices, scale, rows, max_elems, O, L):
-    Hq, Hkv = q.shape[1], k.shape[1]
-    for a, b, w0, w1, mask in _row_batches(rows, slices, max_elems):
-        if w1 <= w0:
-            continue
-        nonempty = mask.any(axis=1)
-        for h in range(Hq):
-            g = _kv_head(h, Hq, Hkv)
-            S = scale * (q[rows[a:b], h, :] @ k[w0:w1, g, :].T)
-            S = np.where(mask, S, -np.inf)
-            m = np.where(nonempty, S.max(axis=1, initial=-np.inf), 0.0)
-            lse = m + np.log(np.exp(S - m[:, None]).sum(axis=1))      # pass 1
-            P = np.where(mask, np.exp(S - np.where(nonempty, lse, 0.0)[:, None]), 0.0)
-            O[a:b, h, :] = P @ v[w0:w1, g, :]                              # pass 2
-            L[h, a:b] = np.where(nonempty, lse, -np.inf)
-
-
-def backward(q, k, v, do, slices: Sequence, scale: float = None, max_elems: int = 1 << 22):
-    """dQ, dK, dV (float64), the textbook gradient of ``forward`` over all rows.
+def backward(q, k, v, do, slices: Sequence, scale: float = None, max_elems: int = 1 << 25):
+    """dQ, dK, dV (float64 ndarrays), the textbook gradient of ``forward``.
 
       P_ij = exp(s_ij - LSE_i) on J_i (0 elsewhere);  D_i = dO_i . O_i;
       dS_ij = P_ij (dO_i . v_j - D_i);
       dQ_i = scale sum_j dS_ij k_j;  dK_j = scale sum_{h in group} sum_i dS_ij q_i;
       dV_j = sum_{h in group} sum_i P_ij dO_i.
     O and LSE are recomputed here in float64."""
-    q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
+    import torch
     Tq, Hq, d = q.shape
     Tk, Hkv = k.shape[0], k.shape[1]
+    G = Hq // Hkv
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     rows = np.arange(Tq)
-    dq = np.zeros_like(q)
-    dk = np.zeros_like(k)
-    dv = np.zeros_like(v)
-    with np.errstate(divide="ignore", invalid="ignore"):
-        _backward_batches(q, k, v, do, slices, scale, rows, max_elems, dq, dk, dv)
-    return dq, dk, dv
+    batches = list(_row_batches(rows, slices, max(1, max_elems // G)))
+    dq = torch.zeros(Tq, Hq, d, dtype=torch.float64)
+    dk = torch.zeros(Tk, Hkv, d, dtype=torch.float64)
+    dv = torch.zeros(Tk, Hkv, d, dtype=torch.float64)
+    for g in range(Hkv):
+        hs = slice(g * G, (g + 1) * G)
+        dKg = torch.zeros(Tk, d, dtype=torch.float64)
+        dVg = torch.zeros(Tk, d, dtype=torch.float64)
+        for a, b, w0, w1, mask in batches:
+            if w1 <= w0:
+                continue
+            Qb, dOb = _f64(q[a:b, hs, :]), _f64(do[a:b, hs, :])
+            Kw, Vw = _f64(k[w0:w1, g, :]), _f64(v[w0:w1, g, :])
+            _, P, Ob = _attend(Qb, Kw, Vw, torch.from_numpy(mask), scale)
+            B = b - a
+            D = (dOb * Ob).sum(dim=-1, keepdim=True)                        # [B, G, 1]
+            dP = (dOb.reshape(B * G, d) @ Vw.T).view(B, G, -1)
+            dS = P * (dP - D)
+            dq[a:b, hs, :] = scale * (dS.reshape(B * G, -1) @ Kw).view(B, G, d)
+            dKg[w0:w1] += scale * (dS.reshape(B * G, -1).T @ Qb.reshape(B * G, d))
+            dVg[w0:w1] += P.reshape(B * G, -1).T @ dOb.reshape(B * G, d)
+        dk[:, g, :] = dKg
+        dv[:, g, :] = dVg
+    return dq.numpy(), dk.numpy(), dv.numpy()
 
 
-def _backward_batches(q, k, v, do, slices, scale, rows, max_elems, dq, dk, dv):
-    Hq, Hkv = q.shape[1], k.shape[1]
-    for a, b, w0, w1, mask in _row_batches(rows, slices, max_elems):
-        if w1 <= w0:
-            continue
-        nonempty = mask.any(axis=1)
-        for h in range(Hq):
-            g = _kv_head(h, Hq, Hkv)
-            Kw, Vw = k[w0:w1, g, :], v[w0:w1, g, :]
-            S = scale * (q[a:b, h, :] @ Kw.T)
-            Sm = np.where(mask, S, -np.inf)
-            m = np.where(nonempty, Sm.max(axis=1, initial=-np.inf), 0.0)
-            lse = m + np.log(np.exp(Sm - m[:, None]).sum(axis=1))
-            P = np.where(mask, np.exp(S - np.where(nonempty, lse, 0.0)[:, None]), 0.0)
-            O = P @ Vw
-            D = (do[a:b, h, :] * O).sum(axis=1)
-            dP = do[a:b, h, :] @ Vw.T
-            dS = P * (dP - D[:, None])
-            dq[a:b, h, :] = scale * (dS @ Kw)
-            dk[w0:w1, g, :] += scale * (dS.T @ q[a:b, h, :])
-            dv[w0:w1, g, :] += P.T @ do[a:b, h, :]
-
-
-def backward_dq_rows(q, k, v, do, slices: Sequence, rows, scale: float = None,
-                     max_elems: int = 1 << 22):
-    """dQ for the given rows only (each row needs only its own O_i and LSE_i)."""
-    q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
+def forward_backward_rows(q, k, v, do, slices: Sequence, rows, scale: float = None,
+                          max_elems: int = 1 << 25):
+    """O, LSE and dQ for the given rows only, in one pass (each row needs only
+    its own valid keys, O_i and LSE_i).  Returns O [n, Hq, d], LSE [Hq, n],
+    dQ [n, Hq, d] as float64 ndarrays."""
+    import torch
     Tq, Hq, d = q.shape
     Hkv = k.shape[1]
+    G = Hq // Hkv
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     rows = np.asarray(rows, dtype=np.int64)
-    out = np.zeros((len(rows), Hq, d))
-    with np.errstate(divide="ignore", invalid="ignore"):
-        _dq_batches(q, k, v, do, slices, scale, rows, max_elems, out)
-    return out
+    rows_t = torch.from_numpy(rows)
+    batches = list(_row_batches(rows, slices, max(1, max_elems // G)))
+    O = torch.zeros(len(rows), Hq, d, dtype=torch.float64)
+    L = torch.full((Hq, len(rows)), -math.inf, dtype=torch.float64)
+    dQ = torch.zeros(len(rows), Hq, d, dtype=torch.float64)
+    for g in range(Hkv):
+        hs = slice(g * G, (g + 1) * G)
+        for a, b, w0, w1, mask in batches:
+            if w1 <= w0:
+                continue
+            Qb, dOb = _f64(q[rows_t[a:b], hs, :]), _f64(do[rows_t[a:b], hs, :])
+            Kw, Vw = _f64(k[w0:w1, g, :]), _f64(v[w0:w1, g, :])
+            lse, P, Ob = _attend(Qb, Kw, Vw, torch.from_numpy(mask), scale)
+            B = b - a
+            D = (dOb * Ob).sum(dim=-1, keepdim=True)
+            dS = P * ((dOb.reshape(B * G, d) @ Vw.T).view(B, G, -1) - D)
+            O[a:b, hs, :] = Ob
+            L[hs, a:b] = lse.T
+            dQ[a:b, hs, :] = scale * (dS.reshape(B * G, -1) @ Kw).view(B, G, d)
+    return O.numpy(), L.numpy(), dQ.numpy()
 
 
-def _dq_batches(q, k, v, do, slices, scale, rows, max_elems, out):
-    Hq, Hkv = q.shape[1], k.shape[1]
-    for a, b, w0, w1, mask in _row_batches(rows, slices, max_elems):
-        if w1 <= w0:
-            continue
-        nonempty = mask.any(axis=1)
-        for h in range(Hq):
-            g = _kv_head(h, Hq, Hkv)
-            Kw, Vw = k[w0:w1, g, :], v[w0:w1, g, :]
-            S = scale * (q[rows[a:b], h, :] @ Kw.T)
-            Sm = np.where(mask, S, -np.inf)
-            m = np.where(nonempty, Sm.max(axis=1, initial=-np.inf), 0.0)
-            lse = m + np.log(np.exp(Sm - m[:, None]).sum(axis=1))
-            P = np.where(mask, np.exp(S - np.where(nonempty, lse, 0.0)[:, None]), 0.0)
-            O = P @ Vw
-            D = (do[rows[a:b], h, :] * O).sum(axis=1)
-            dS = P * (do[rows[a:b], h, :] @ Vw.T - D[:, None])
-            out[a:b, h, :] = scale * (dS @ Kw)
+def backward_dq_rows(q, k, v, do, slices: Sequence, rows, scale: float = None,
+                     max_elems: int = 1 << 25):
+    """dQ for the given rows only."""
+    return forward_backward_rows(q, k, v, do, slices, rows, scale, max_elems)[2]
 
 
 def lse_merge(o1, lse1, o2, lse2):
