@@ -72,7 +72,7 @@ __global__ __launch_bounds__(NT, 1) void ffa_bwd_dkdv_kernel(BwdArgs a) {
   constexpr int KS = D / 16;
 
   const MetaView mv = meta_view(a.meta);
-  const MetaHeader* hd = mv.hdr;
+  const FFA_CONST MetaHeader* hd = mv.hdr;
   if (hd->status != 0 || hd->seqlen_q != a.Tq || hd->seqlen_k != a.Tk) return;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -87,8 +87,8 @@ __global__ __launch_bounds__(NT, 1) void ffa_bwd_dkdv_kernel(BwdArgs a) {
   const int f0 = mv.kf_off[n], nF = mv.kf_off[n + 1] - f0;
   const int p0 = mv.km_off[n], nP = mv.km_off[n + 1] - p0;
   const int nT = nP + nF;
-  const int32_t* fidx = mv.var + hd->list_off[L_KF] + f0;
-  const int32_t* pidx = mv.var + hd->list_off[L_KM] + p0;
+  cint32_t* fidx = mv.var + hd->list_off[L_KF] + f0;
+  cint32_t* pidx = mv.var + hd->list_off[L_KM] + p0;
 
   // K and V as B operands: lane holds K[key][16k + 8*h32 + e]
   bf16x8 kop[KS], vop[KS];
@@ -103,6 +103,8 @@ __global__ __launch_bounds__(NT, 1) void ffa_bwd_dkdv_kernel(BwdArgs a) {
       __builtin_memcpy(&vop[k], &w, 16);
     }
   }
+
+  wait_vmem();
 
   // loop-invariant LDS addresses
   int raddr[KS];                 // 128-bit row reads (row l32, chunk 2k + h32)
@@ -142,10 +144,8 @@ __global__ __launch_bounds__(NT, 1) void ffa_bwd_dkdv_kernel(BwdArgs a) {
     if (wid < 2) {
       const float* src = (wid == 0 ? a.lvec : a.dvec) + (int64_t)hq * a.Tq + m * BM_B;
       const int rows = vr < 0 ? 0 : (vr > BM_B ? BM_B : vr);
-      const __amdgpu_buffer_rsrc_t r = make_rsrc(src, (uint32_t)(rows * 4));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          r, (__attribute__((address_space(3))) void*)(st + 2 * TILE_B + wid * BM_B * 4), 4,
-          lane * 4, 0, 0, 0);
+      const i32x4 r = make_rsrc(src, (uint32_t)(rows * 4));
+      dma4(r, st + 2 * TILE_B + wid * BM_B * 4, lane * 4);
     }
   };
   const float c = a.scale_log2;
@@ -186,7 +186,7 @@ __global__ __launch_bounds__(NT, 1) void ffa_bwd_dkdv_kernel(BwdArgs a) {
       const int m0 = m * BM_B;
       const int mf = m0 / BM_F;
       const int s0 = mv.qs_off[mf], nS = mv.qs_off[mf + 1] - s0;
-      const int32_t* sidx = mv.var + hd->list_off[L_QS] + s0;
+      cint32_t* sidx = mv.var + hd->list_off[L_QS] + s0;
       mk = 0;
       for (int si = 0; si < nS; ++si) {
         const Slice sl = load_slice(mv.slices, sidx[si]);
@@ -244,10 +244,12 @@ __global__ __launch_bounds__(NT, 1) void ffa_bwd_dkdv_kernel(BwdArgs a) {
         dkacc[mb] = mfma32(qa, sb, dkacc[mb]);
       }
     }
+    wait_dma();
     __syncthreads();
   };
 
   if (total > 0) issue(0, 0);
+  wait_dma();
   __syncthreads();
   for (int u = 0; u < total; u += 2) {
     tile(std::integral_constant<int, 0>{}, u);
@@ -286,7 +288,7 @@ __global__ __launch_bounds__(NT, 1) void ffa_bwd_dq_kernel(BwdArgs a) {
   constexpr int KS = D / 16;
 
   const MetaView mv = meta_view(a.meta);
-  const MetaHeader* hd = mv.hdr;
+  const FFA_CONST MetaHeader* hd = mv.hdr;
   if (hd->status != 0 || hd->seqlen_q != a.Tq || hd->seqlen_k != a.Tk) return;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -301,10 +303,10 @@ __global__ __launch_bounds__(NT, 1) void ffa_bwd_dq_kernel(BwdArgs a) {
   const int f0 = mv.qf_off[m], nF = mv.qf_off[m + 1] - f0;
   const int p0 = mv.qm_off[m], nP = mv.qm_off[m + 1] - p0;
   const int nT = nP + nF;
-  const int32_t* fidx = mv.var + hd->list_off[L_QF] + f0;
-  const int32_t* pidx = mv.var + hd->list_off[L_QM] + p0;
+  cint32_t* fidx = mv.var + hd->list_off[L_QF] + f0;
+  cint32_t* pidx = mv.var + hd->list_off[L_QM] + p0;
   const int s0 = mv.qs_off[m], nS = mv.qs_off[m + 1] - s0;
-  const int32_t* sidx = mv.var + hd->list_off[L_QS] + s0;
+  cint32_t* sidx = mv.var + hd->list_off[L_QS] + s0;
 
   bf16x8 qop[KS], gop[KS];
   {
@@ -323,6 +325,7 @@ __global__ __launch_bounds__(NT, 1) void ffa_bwd_dq_kernel(BwdArgs a) {
     l2 = a.lvec[(int64_t)head * a.Tq + qrow];
     dval = a.dvec[(int64_t)head * a.Tq + qrow];
   }
+  wait_vmem();
 
   int raddr[KS];
 #pragma unroll
@@ -425,10 +428,12 @@ __global__ __launch_bounds__(NT, 1) void ffa_bwd_dq_kernel(BwdArgs a) {
         dqacc[mb] = mfma32(ka, sb, dqacc[mb]);
       }
     }
+    wait_dma();
     __syncthreads();
   };
 
   if (nT > 0) issue(0, 0);
+  wait_dma();
   __syncthreads();
   for (int t = 0; t < nT; t += 2) {
     tile(std::integral_constant<int, 0>{}, t);

@@ -34,7 +34,7 @@ __global__ __launch_bounds__(NT, 2) void ffa_fwd_kernel(FwdArgs a) {
   constexpr int KS = D / 16;                    // 16-wide d steps of S^T
 
   const MetaView mv = meta_view(a.meta);
-  const MetaHeader* hd = mv.hdr;
+  const FFA_CONST MetaHeader* hd = mv.hdr;
   if (hd->status != 0 || hd->seqlen_q != a.Tq || hd->seqlen_k != a.Tk) return;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -49,10 +49,10 @@ __global__ __launch_bounds__(NT, 2) void ffa_fwd_kernel(FwdArgs a) {
   const int f0 = mv.qf_off[m], nF = mv.qf_off[m + 1] - f0;
   const int p0 = mv.qm_off[m], nP = mv.qm_off[m + 1] - p0;
   const int nT = nP + nF;
-  const int32_t* fidx = mv.var + hd->list_off[L_QF] + f0;
-  const int32_t* pidx = mv.var + hd->list_off[L_QM] + p0;
+  cint32_t* fidx = mv.var + hd->list_off[L_QF] + f0;
+  cint32_t* pidx = mv.var + hd->list_off[L_QM] + p0;
   const int s0 = mv.qs_off[m], nS = mv.qs_off[m + 1] - s0;
-  const int32_t* sidx = mv.var + hd->list_off[L_QS] + s0;
+  cint32_t* sidx = mv.var + hd->list_off[L_QS] + s0;
 
   // Q^T operand: lane holds Q[qrow][16k + 8*h32 + e]
   bf16x8 qop[KS];
@@ -64,6 +64,8 @@ __global__ __launch_bounds__(NT, 2) void ffa_fwd_kernel(FwdArgs a) {
       __builtin_memcpy(&qop[k], &u, 16);
     }
   }
+
+  wait_vmem();
 
   // loop-invariant LDS read addresses (stage, key block and chunk offsets
   // are added as immediates)
@@ -192,10 +194,12 @@ __global__ __launch_bounds__(NT, 2) void ffa_fwd_kernel(FwdArgs a) {
         oacc[mb] = mfma32(vop, pop, oacc[mb]);
       }
     }
+    wait_dma();
     __syncthreads();
   };
 
   if (nT > 0) issue(0, 0);
+  wait_dma();
   __syncthreads();
   for (int t = 0; t < nT; t += 2) {
     tile(std::integral_constant<int, 0>{}, t);

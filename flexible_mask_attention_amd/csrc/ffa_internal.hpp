@@ -84,35 +84,44 @@ inline MetaLayout meta_layout(int32_t S, int32_t Tq, int32_t Tk) {
   return L;
 }
 
-// Device view of a built metadata buffer.
+// Device view of a built metadata buffer, read through the constant address
+// space: the buffer does not change while forward / backward kernels run, so
+// uniform reads of it become scalar loads.
+#define FFA_CONST __attribute__((address_space(4)))
+typedef const FFA_CONST int32_t cint32_t;
+
 struct MetaView {
-  const MetaHeader* hdr;
-  const int32_t* slices;
-  const int32_t* qf_off;
-  const int32_t* qm_off;
-  const int32_t* kf_off;
-  const int32_t* km_off;
-  const int32_t* qs_off;
-  const int32_t* sched_f;
-  const int32_t* sched_b;
-  const int32_t* var;
+  const FFA_CONST MetaHeader* hdr;
+  cint32_t* slices;
+  cint32_t* qf_off;
+  cint32_t* qm_off;
+  cint32_t* kf_off;
+  cint32_t* km_off;
+  cint32_t* qs_off;
+  cint32_t* sched_f;
+  cint32_t* sched_b;
+  cint32_t* var;
 };
 
 __device__ inline MetaView meta_view(const void* meta) {
   MetaView v;
-  const char* b = reinterpret_cast<const char*>(meta);
-  v.hdr = reinterpret_cast<const MetaHeader*>(b);
-  v.slices = reinterpret_cast<const int32_t*>(b + v.hdr->byte_off[A_SLICES]);
-  v.qf_off = reinterpret_cast<const int32_t*>(b + v.hdr->byte_off[A_QF_OFF]);
-  v.qm_off = reinterpret_cast<const int32_t*>(b + v.hdr->byte_off[A_QM_OFF]);
-  v.kf_off = reinterpret_cast<const int32_t*>(b + v.hdr->byte_off[A_KF_OFF]);
-  v.km_off = reinterpret_cast<const int32_t*>(b + v.hdr->byte_off[A_KM_OFF]);
-  v.qs_off = reinterpret_cast<const int32_t*>(b + v.hdr->byte_off[A_QS_OFF]);
-  v.sched_f = reinterpret_cast<const int32_t*>(b + v.hdr->byte_off[A_SCHED_F]);
-  v.sched_b = reinterpret_cast<const int32_t*>(b + v.hdr->byte_off[A_SCHED_B]);
-  v.var = reinterpret_cast<const int32_t*>(b + v.hdr->byte_off[A_VAR]);
+  const FFA_CONST char* b = (const FFA_CONST char*)(meta);
+  v.hdr = (const FFA_CONST MetaHeader*)(b);
+  v.slices = (cint32_t*)(b + v.hdr->byte_off[A_SLICES]);
+  v.qf_off = (cint32_t*)(b + v.hdr->byte_off[A_QF_OFF]);
+  v.qm_off = (cint32_t*)(b + v.hdr->byte_off[A_QM_OFF]);
+  v.kf_off = (cint32_t*)(b + v.hdr->byte_off[A_KF_OFF]);
+  v.km_off = (cint32_t*)(b + v.hdr->byte_off[A_KM_OFF]);
+  v.qs_off = (cint32_t*)(b + v.hdr->byte_off[A_QS_OFF]);
+  v.sched_f = (cint32_t*)(b + v.hdr->byte_off[A_SCHED_F]);
+  v.sched_b = (cint32_t*)(b + v.hdr->byte_off[A_SCHED_B]);
+  v.var = (cint32_t*)(b + v.hdr->byte_off[A_VAR]);
   return v;
 }
+
+// Wait until this wave's vector-memory loads issued so far (by compiled
+// code) have returned; the compiler tracks this builtin, unlike wait_dma.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // ---------------------------------------------------------------------------
 // Slice intervals.  For slice (q0,q1,k0,k1,t) the valid keys of query row i
@@ -124,7 +133,8 @@ struct Slice {
   int32_t q0, q1, k0, k1, t;
 };
 
-__device__ __forceinline__ Slice load_slice(const int32_t* s, int idx) {
+template <typename P>
+__device__ __forceinline__ Slice load_slice(P s, int idx) {
   Slice r;
   r.q0 = s[5 * idx + 0];
   r.q1 = s[5 * idx + 1];
@@ -253,20 +263,38 @@ __device__ __forceinline__ bf16x8 read_row_operand(const char* tile, int r, int 
   return v;
 }
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
 // Buffer resource over [base, base + num_bytes): loads past the end return 0.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {
-  // the arguments are wave-uniform; keep them in scalar registers so the
-  // descriptor is an SGPR quad (no per-lane waterfall around the loads)
-  const int n = __builtin_amdgcn_readfirstlane((int)num_bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
+// All fields are wave-uniform and kept in scalar registers.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t num_bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((p >> 32) & 0xffffu));   // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane((int)num_bytes);
+  r[3] = 0x00020000;
+  return r;
 }
 
-// 16 bytes per lane from global straight into LDS: lane l writes
-// lds_base + 16*l (lds_base must be wave-uniform).
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds_base, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16,
-                                           (int)voff, 0, 0, 0);
+// 16 (or 4) bytes per lane from global straight into LDS: lane l writes
+// lds_base + 16*l (4*l).  Issued as inline assembly so that the compiler does
+// not make later LDS reads of the *other* buffer wait for these loads; the
+// caller waits explicitly (wait_dma) before the barrier that publishes them.
+__device__ __forceinline__ void dma16(const i32x4& r, char* lds_base, uint32_t voff) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(size_t)((__attribute__((address_space(3))) char*)lds_base));
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(m0), "v"(voff), "s"(r) : "memory", "m0");
 }
+__device__ __forceinline__ void dma4(const i32x4& r, char* lds_base, uint32_t voff) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(size_t)((__attribute__((address_space(3))) char*)lds_base));
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :: "s"(m0), "v"(voff), "s"(r) : "memory", "m0");
+}
+// all of this wave's global->LDS loads have landed
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Per-lane byte offsets for loading a [ROWS][D] bf16 tile whose rows are
 // `ts_bytes` apart in global memory into the swizzled LDS layout with 16-byte
@@ -297,7 +325,7 @@ struct TileDma {
                                        int valid_rows, char* lds_tile) const {
     const __bf16* b = head_base + (int64_t)row_base * ts_elems;
     const int vr = valid_rows < 0 ? 0 : (valid_rows > ROWS ? ROWS : valid_rows);
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(b, (uint32_t)(vr * ts_elems * 2));
+    const i32x4 r = make_rsrc(b, (uint32_t)(vr * ts_elems * 2));
 #pragma unroll
     for (int i = 0; i < NL; ++i) dma16(r, lds_tile + (row0 + i * RPL) * ROWB, voff[i]);
   }
