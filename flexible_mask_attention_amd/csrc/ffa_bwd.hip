@@ -279,7 +279,7 @@ __global__ __launch_bounds__(NT, 1) void ffa_bwd_dkdv_kernel(BwdArgs a) {
 // dQ: owner (query head, BM_F-row block), 4 waves x 32 rows, q2k tiles.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(NT, 1) void ffa_bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NT, 2) void ffa_bwd_dq_kernel(BwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int TILE_B = BN_F * D * 2;
   constexpr int STAGE_B = 2 * TILE_B;
