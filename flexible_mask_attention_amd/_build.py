@@ -19,6 +19,9 @@ FLAGS = [
     "-fvisibility=hidden", "-Wall", "-Wno-unused-function",
     # keep the compiler from forming packed fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: avoids per-tile copies between the
+    # accumulation registers and the VGPRs that the softmax arithmetic reads
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

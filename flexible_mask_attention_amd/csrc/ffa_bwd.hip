@@ -63,7 +63,7 @@ __global__ __launch_bounds__(NT) void ffa_bwd_pre_kernel(BwdArgs a) {
 // dK, dV: owner (kv head, BN_B-key block), 4 waves x 32 keys.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(NT, 1) void ffa_bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NT, 2) void ffa_bwd_dkdv_kernel(BwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int TILE_B = BM_B * D * 2;          // bytes of one Q or dO tile
   constexpr int STAGE_B = 2 * TILE_B + 2 * BM_B * 4;
@@ -106,19 +106,16 @@ __global__ __launch_bounds__(NT, 1) void ffa_bwd_dkdv_kernel(BwdArgs a) {
 
   wait_vmem();
 
-  // loop-invariant LDS addresses
-  int raddr[KS];                 // 128-bit row reads (row l32, chunk 2k + h32)
+  // loop-invariant LDS read bases: the 128-bit read of chunk 2k + h32 of row
+  // l32 is at (k / 2) * GB + raddr[k % 2], the transposed read of rows 8j..
+  // of column group mb at mb * GB + taddr[j] (row offsets are immediates)
+  constexpr int GB = group_bytes<BM_B>();
+  int raddr[2], taddr[2];
 #pragma unroll
-  for (int k = 0; k < KS; ++k) raddr[k] = lds_off<D>(l32, 2 * k + h32);
-  int taddr[MB][2];              // transposed reads (rows 4*h32 + t/4 (+8), cols 32mb + ...)
+  for (int p = 0; p < 2; ++p) raddr[p] = lds_pos(l32, 2 * p + h32);
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int rr = 4 * h32 + (t16 >> 2) + 8 * j;
-      const int cc = 32 * mb + 16 * (g16 & 1) + 4 * (t16 & 3);
-      taddr[mb][j] = lds_off<D>(rr, cc >> 3) + ((cc & 7) << 1);
-    }
+  for (int j = 0; j < 2; ++j)
+    taddr[j] = lds_pos(4 * h32 + (t16 >> 2) + 8 * j, 2 * (g16 & 1) + ((t16 >> 1) & 1)) + 8 * (t16 & 1);
   const int laddr = 2 * TILE_B + 16 * h32;   // row-stat reads: + (32qb + 8j) * 4
 
   TileDma<D, BM_B> dq_dma, dg_dma;
@@ -159,35 +156,14 @@ __global__ __launch_bounds__(NT, 1) void ffa_bwd_dkdv_kernel(BwdArgs a) {
     const __attribute__((address_space(3))) char* lb =
         (const __attribute__((address_space(3))) char*)smem + stage * STAGE_B;
 
-    // S = Q K^T and dP = dO V^T; lane = key, registers = rows 32qb + 8(r/4) + 4*h32 + r%4
-    f32x16 sacc[QB], pacc[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      sacc[qb] = f32x16{};
-      pacc[qb] = f32x16{};
-    }
-#pragma unroll
-    for (int k = 0; k < KS; ++k)
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        bf16x8 qa, ga;
-        u32x4 u1 = *(const __attribute__((address_space(3))) u32x4*)(lb + raddr[k] + qb * 32 * D * 2);
-        u32x4 u2 = *(const __attribute__((address_space(3))) u32x4*)(lb + TILE_B + raddr[k] + qb * 32 * D * 2);
-        __builtin_memcpy(&qa, &u1, 16);
-        __builtin_memcpy(&ga, &u2, 16);
-        sacc[qb] = mfma32(qa, kop[k], sacc[qb]);
-        pacc[qb] = mfma32(ga, vop[k], pacc[qb]);
-      }
-
-    uint64_t mk = ~0ull;
+    // Partial tile: valid rows of this key inside [m0, m0 + BM_B) from the
+    // slices of the enclosing forward query block, one bit per row
+    uint64_t mk = 0;
     if (masked) {
-      // valid rows of this key inside [m0, m0 + BM_B), from the slices of the
-      // enclosing forward query block
       const int m0 = m * BM_B;
       const int mf = m0 / BM_F;
       const int s0 = mv.qs_off[mf], nS = mv.qs_off[mf + 1] - s0;
       cint32_t* sidx = mv.var + hd->list_off[L_QS] + s0;
-      mk = 0;
       for (int si = 0; si < nS; ++si) {
         const Slice sl = load_slice(mv.slices, sidx[si]);
         int lo, hi;
@@ -199,9 +175,29 @@ __global__ __launch_bounds__(NT, 1) void ffa_bwd_dkdv_kernel(BwdArgs a) {
       mk >>= 4 * h32;
     }
 
+    // one 32-row half at a time, so that only one S / dP pair is live
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const uint32_t w = static_cast<uint32_t>(mk >> (32 * qb));
+      // S = Q K^T and dP = dO V^T; lane = key, registers = rows 32qb + 8(r/4) + 4*h32 + r%4
+      f32x16 sacc = f32x16{}, pacc = f32x16{};
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        bf16x8 qa, ga;
+        u32x4 u1 = *(const __attribute__((address_space(3))) u32x4*)(lb + (k >> 1) * GB + raddr[k & 1] + qb * 32 * 64);
+        u32x4 u2 = *(const __attribute__((address_space(3))) u32x4*)(lb + TILE_B + (k >> 1) * GB + raddr[k & 1] + qb * 32 * 64);
+        __builtin_memcpy(&qa, &u1, 16);
+        __builtin_memcpy(&ga, &u2, 16);
+        sacc = mfma32(qa, kop[k], sacc);
+        pacc = mfma32(ga, vop[k], pacc);
+      }
+      if (masked) {
+        const uint32_t w = static_cast<uint32_t>(mk >> (32 * qb));
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (!((w >> (8 * (r >> 2) + (r & 3))) & 1u)) sacc[r] = -INFINITY;
+      }
+
+      // P = exp2(S c - LSE log2 e), dS = P (dP - D)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int ro = laddr + (32 * qb + 8 * j) * 4;
@@ -210,38 +206,36 @@ __global__ __launch_bounds__(NT, 1) void ffa_bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 4 * j + i;
-          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][r], c, -l4[i]));
-          if (masked && !((w >> (8 * j + i)) & 1u)) pv = 0.f;
-          sacc[qb][r] = pv;
-          pacc[qb][r] = pv * (pacc[qb][r] - d4[i]);
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -l4[i]));
+          sacc[r] = pv;
+          pacc[r] = pv * (pacc[r] - d4[i]);
         }
       }
-    }
 
-    // dV^T += dO^T P and dK^T += Q^T dS over 16-row chunks
+      // dV^T += dO^T P and dK^T += Q^T dS over the half's two 16-row chunks
 #pragma unroll
-    for (int cc = 0; cc < BM_B / 16; ++cc) {
-      const int qb = cc >> 1, c2 = cc & 1;
-      bf16x8 pb, sb;
+      for (int c2 = 0; c2 < 2; ++c2) {
+        bf16x8 pb, sb;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pb[e] = static_cast<__bf16>(sacc[qb][8 * c2 + e]);
-        sb[e] = static_cast<__bf16>(pacc[qb][8 * c2 + e]);
-      }
-      const int roff = (32 * qb + 16 * c2) * D * 2;
+        for (int e = 0; e < 8; ++e) {
+          pb[e] = static_cast<__bf16>(sacc[8 * c2 + e]);
+          sb[e] = static_cast<__bf16>(pacc[8 * c2 + e]);
+        }
+        const int roff = (32 * qb + 16 * c2) * 64;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const i16x4 g0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lb + TILE_B + taddr[mb][0] + roff));
-        const i16x4 g1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lb + TILE_B + taddr[mb][1] + roff));
-        const i16x4 q0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lb + taddr[mb][0] + roff));
-        const i16x4 q1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lb + taddr[mb][1] + roff));
-        const i16x8 gg = __builtin_shufflevector(g0, g1, 0, 1, 2, 3, 4, 5, 6, 7);
-        const i16x8 qq = __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7);
-        bf16x8 ga, qa;
-        __builtin_memcpy(&ga, &gg, 16);
-        __builtin_memcpy(&qa, &qq, 16);
-        dvacc[mb] = mfma32(ga, pb, dvacc[mb]);
-        dkacc[mb] = mfma32(qa, sb, dkacc[mb]);
+        for (int mb = 0; mb < MB; ++mb) {
+          const i16x4 g0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lb + TILE_B + mb * GB + taddr[0] + roff));
+          const i16x4 g1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lb + TILE_B + mb * GB + taddr[1] + roff));
+          const i16x4 q0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lb + mb * GB + taddr[0] + roff));
+          const i16x4 q1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lb + mb * GB + taddr[1] + roff));
+          const i16x8 gg = __builtin_shufflevector(g0, g1, 0, 1, 2, 3, 4, 5, 6, 7);
+          const i16x8 qq = __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7);
+          bf16x8 ga, qa;
+          __builtin_memcpy(&ga, &gg, 16);
+          __builtin_memcpy(&qa, &qq, 16);
+          dvacc[mb] = mfma32(ga, pb, dvacc[mb]);
+          dkacc[mb] = mfma32(qa, sb, dkacc[mb]);
+        }
       }
     }
     wait_dma();
@@ -327,18 +321,13 @@ __global__ __launch_bounds__(NT, 2) void ffa_bwd_dq_kernel(BwdArgs a) {
   }
   wait_vmem();
 
-  int raddr[KS];
+  constexpr int GB = group_bytes<BN_F>();
+  int raddr[2], taddr[2];
 #pragma unroll
-  for (int k = 0; k < KS; ++k) raddr[k] = lds_off<D>(l32, 2 * k + h32);
-  int taddr[MB][2];
+  for (int p = 0; p < 2; ++p) raddr[p] = lds_pos(l32, 2 * p + h32);
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int rr = 4 * h32 + (t16 >> 2) + 8 * j;
-      const int cc = 32 * mb + 16 * (g16 & 1) + 4 * (t16 & 3);
-      taddr[mb][j] = lds_off<D>(rr, cc >> 3) + ((cc & 7) << 1);
-    }
+  for (int j = 0; j < 2; ++j)
+    taddr[j] = lds_pos(4 * h32 + (t16 >> 2) + 8 * j, 2 * (g16 & 1) + ((t16 >> 1) & 1)) + 8 * (t16 & 1);
 
   TileDma<D, BN_F> dmk, dmv;
   dmk.init(wid, lane, a.k_ts);
@@ -377,18 +366,17 @@ __global__ __launch_bounds__(NT, 2) void ffa_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         bf16x8 ka, va;
-        u32x4 u1 = *(const __attribute__((address_space(3))) u32x4*)(lb + raddr[k] + kb * 32 * D * 2);
-        u32x4 u2 = *(const __attribute__((address_space(3))) u32x4*)(lb + TILE_B + raddr[k] + kb * 32 * D * 2);
+        u32x4 u1 = *(const __attribute__((address_space(3))) u32x4*)(lb + (k >> 1) * GB + raddr[k & 1] + kb * 32 * 64);
+        u32x4 u2 = *(const __attribute__((address_space(3))) u32x4*)(lb + TILE_B + (k >> 1) * GB + raddr[k & 1] + kb * 32 * 64);
         __builtin_memcpy(&ka, &u1, 16);
         __builtin_memcpy(&va, &u2, 16);
         sacc[kb] = mfma32(ka, qop[k], sacc[kb]);
         pacc[kb] = mfma32(va, gop[k], pacc[kb]);
       }
 
-    uint64_t mk = ~0ull;
     if (masked) {
       const int n0 = n * BN_F;
-      mk = 0;
+      uint64_t mk = 0;
       for (int si = 0; si < nS; ++si) {
         const Slice sl = load_slice(mv.slices, sidx[si]);
         int lo, hi;
@@ -398,18 +386,22 @@ __global__ __launch_bounds__(NT, 2) void ffa_bwd_dq_kernel(BwdArgs a) {
         if (lo <= hi) mk |= bit_range(lo - n0, hi - n0);
       }
       mk >>= 4 * h32;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const uint32_t w = static_cast<uint32_t>(mk >> (32 * kb));
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (!((w >> (8 * (r >> 2) + (r & 3))) & 1u)) sacc[kb][r] = -INFINITY;
+      }
     }
 
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const uint32_t w = static_cast<uint32_t>(mk >> (32 * kb));
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], c, -l2));
-        if (masked && !((w >> (8 * (r >> 2) + (r & 3))) & 1u)) pv = 0.f;
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], c, -l2));
         pacc[kb][r] = pv * (pacc[kb][r] - dval);
       }
-    }
 
 #pragma unroll
     for (int cc = 0; cc < BN_F / 16; ++cc) {
@@ -417,11 +409,11 @@ __global__ __launch_bounds__(NT, 2) void ffa_bwd_dq_kernel(BwdArgs a) {
       bf16x8 sb;
 #pragma unroll
       for (int e = 0; e < 8; ++e) sb[e] = static_cast<__bf16>(pacc[kb][8 * c2 + e]);
-      const int roff = (32 * kb + 16 * c2) * D * 2;
+      const int roff = (32 * kb + 16 * c2) * 64;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        const i16x4 k0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lb + taddr[mb][0] + roff));
-        const i16x4 k1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lb + taddr[mb][1] + roff));
+        const i16x4 k0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lb + mb * GB + taddr[0] + roff));
+        const i16x4 k1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lb + mb * GB + taddr[1] + roff));
         const i16x8 kk = __builtin_shufflevector(k0, k1, 0, 1, 2, 3, 4, 5, 6, 7);
         bf16x8 ka;
         __builtin_memcpy(&ka, &kk, 16);

@@ -67,20 +67,17 @@ __global__ __launch_bounds__(NT, 2) void ffa_fwd_kernel(FwdArgs a) {
 
   wait_vmem();
 
-  // loop-invariant LDS read addresses (stage, key block and chunk offsets
-  // are added as immediates)
-  int kaddr[KS];
+  // loop-invariant LDS read bases (stage, key block, column group and chunk
+  // offsets are immediates): the 128-bit K read of chunk 2k + h32 is at
+  // (k / 2) * GB + kaddr[k % 2], the transposed V read of rows 8j.. of column
+  // group mb at mb * GB + vaddr[j]
+  constexpr int GB = group_bytes<BN_F>();
+  int kaddr[2], vaddr[2];
 #pragma unroll
-  for (int k = 0; k < KS; ++k) kaddr[k] = lds_off<D>(l32, 2 * k + h32);
-  int vaddr[MB][2];
+  for (int p = 0; p < 2; ++p) kaddr[p] = lds_pos(l32, 2 * p + h32);
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int rr = 4 * h32 + (t16 >> 2) + 8 * j;
-      const int cc = 32 * mb + 16 * (g16 & 1) + 4 * (t16 & 3);
-      vaddr[mb][j] = lds_off<D>(rr, cc >> 3) + ((cc & 7) << 1);
-    }
+  for (int j = 0; j < 2; ++j)
+    vaddr[j] = lds_pos(4 * h32 + (t16 >> 2) + 8 * j, 2 * (g16 & 1) + ((t16 >> 1) & 1)) + 8 * (t16 & 1);
 
   TileDma<D, BN_F> dma;
   dma.init(wid, lane, a.k_ts);
@@ -119,7 +116,7 @@ __global__ __launch_bounds__(NT, 2) void ffa_fwd_kernel(FwdArgs a) {
     for (int k = 0; k < KS; ++k)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        u32x4 u = *(const __attribute__((address_space(3))) u32x4*)(lb + kaddr[k] + kb * 32 * D * 2);
+        u32x4 u = *(const __attribute__((address_space(3))) u32x4*)(lb + (k >> 1) * GB + kaddr[k & 1] + kb * 32 * 64);
         bf16x8 kop;
         __builtin_memcpy(&kop, &u, 16);
         sacc[kb] = mfma32(kop, qop[k], sacc[kb]);
@@ -181,13 +178,13 @@ __global__ __launch_bounds__(NT, 2) void ffa_fwd_kernel(FwdArgs a) {
       bf16x8 pop;
 #pragma unroll
       for (int e = 0; e < 8; ++e) pop[e] = static_cast<__bf16>(sacc[kb][8 * c2 + e]);
-      const int roff = TILE_B + (32 * kb + 16 * c2) * D * 2;
+      const int roff = TILE_B + (32 * kb + 16 * c2) * 64;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4_t*)(lb + vaddr[mb][0] + roff));
+            (lds_i16x4_t*)(lb + mb * GB + vaddr[0] + roff));
         const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4_t*)(lb + vaddr[mb][1] + roff));
+            (lds_i16x4_t*)(lb + mb * GB + vaddr[1] + roff));
         const i16x8 vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
         bf16x8 vop;
         __builtin_memcpy(&vop, &vv, 16);

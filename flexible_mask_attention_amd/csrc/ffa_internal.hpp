@@ -196,72 +196,27 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ bf16x8 pack_bf16x8(const float* x) {
-  bf16x8 r;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = static_cast<__bf16>(x[e]);
-  return r;
-}
-
 // ---------------------------------------------------------------------------
-// LDS tiles of [rows][D] bf16 stored in 16-byte chunks.  Chunk c of row r sits
-// at chunk position c ^ swz(r).  swz keeps both access patterns conflict-free:
-// 16 consecutive rows reading one chunk (128-bit operand reads) and 4
-// consecutive rows x 4 adjacent chunks (transposed 64-bit reads).
+// LDS tiles of [ROWS][D] bf16 are stored as D/32 column groups, each a
+// [ROWS][64 B] block of four 16-byte chunks per row.  Chunk q of row r sits at
+// chunk position q ^ ((r >> 2) & 3) of its row.  This keeps the two read
+// patterns conflict-free: 16 consecutive rows reading one chunk (128-bit
+// operand reads: the rows fall on 4 different 256-byte bank lines, the swizzle
+// spreads each line over 4 chunk positions) and 4 consecutive rows x 64 bytes
+// (transposed 64-bit reads: 256 contiguous bytes).  The swizzle depends only
+// on bits 2..3 of the row, so moving by a multiple of 16 rows or by whole
+// column groups is a constant byte offset, and every operand address is one of
+// two per-lane bases plus an immediate.
 // ---------------------------------------------------------------------------
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128) {
-    return ((r & 3) << 2) | ((r >> 2) & 3);
-  } else {
-    return (((r & 3) << 1) | ((r >> 2) & 1)) & 7;
-  }
-}
+template <int ROWS>
+constexpr int group_bytes() { return ROWS * 64; }
 
-template <int D>
-__device__ __forceinline__ int lds_off(int r, int c) {  // byte offset of chunk c of row r
-  return r * (D * 2) + ((c ^ swz<D>(r)) << 4);
+// byte offset of chunk q (0..3) of row r inside a column group
+__device__ __forceinline__ int lds_pos(int r, int q) {
+  return r * 64 + (((q ^ (r >> 2)) & 3) << 4);
 }
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
-
-// Transposed read: within each 16-lane group, lane t returns column t of the
-// 4 x 16 block of bf16 whose row e is the 32 bytes loaded by lanes 4e..4e+3.
-// Each lane passes the LDS byte address of its own 8-byte piece.
-__device__ __forceinline__ i16x4 ds_read_tr16(const char* lds_base, int byte_off) {
-  const __attribute__((address_space(3))) char* p =
-      (const __attribute__((address_space(3))) char*)(lds_base) + byte_off;
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p);
-}
-
-// 8 bf16 of an MFMA operand whose rows are {r0..r0+3} and {r0+8..r0+11} of a
-// swizzled [rows][D] tile, column `col` (= this lane's output index).
-// lane t of each 16-lane group reads row r0 + t/4 (+8), columns
-// colbase + 4*(t%4) .. +3, where colbase = col - t.
-template <int D>
-__device__ __forceinline__ bf16x8 read_tr_operand(const char* tile, int r0, int colbase, int t) {
-  const int rr = r0 + (t >> 2);
-  const int cc = colbase + 4 * (t & 3);           // first column of this lane's 8-byte piece
-  const int o1 = lds_off<D>(rr, cc >> 3) + ((cc & 7) << 1);
-  const int o2 = lds_off<D>(rr + 8, cc >> 3) + ((cc & 7) << 1);
-  i16x4 a = ds_read_tr16(tile, o1);
-  i16x4 b = ds_read_tr16(tile, o2);
-  bf16x8 r;
-  __builtin_memcpy(&r, &a, 8);
-  __builtin_memcpy(reinterpret_cast<char*>(&r) + 8, &b, 8);
-  return r;
-}
-
-// 128-bit operand read: row r, chunk c of a swizzled tile.
-template <int D>
-__device__ __forceinline__ bf16x8 read_row_operand(const char* tile, int r, int c) {
-  const __attribute__((address_space(3))) char* p =
-      (const __attribute__((address_space(3))) char*)(tile) + lds_off<D>(r, c);
-  bf16x8 v;
-  u32x4 u = *(const __attribute__((address_space(3))) u32x4*)p;
-  __builtin_memcpy(&v, &u, 16);
-  return v;
-}
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
@@ -278,14 +233,15 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t num_bytes)
 }
 
 // 16 (or 4) bytes per lane from global straight into LDS: lane l writes
-// lds_base + 16*l (4*l).  Issued as inline assembly so that the compiler does
-// not make later LDS reads of the *other* buffer wait for these loads; the
-// caller waits explicitly (wait_dma) before the barrier that publishes them.
-__device__ __forceinline__ void dma16(const i32x4& r, char* lds_base, uint32_t voff) {
+// lds_base + 16*l (4*l); the global address is base + voff + soff, soff being
+// wave-uniform.  Issued as inline assembly so that the compiler does not make
+// later LDS reads of the *other* buffer wait for these loads; the caller
+// waits explicitly (wait_dma) before the barrier that publishes them.
+__device__ __forceinline__ void dma16(const i32x4& r, char* lds_base, uint32_t voff, uint32_t soff) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(
       (uint32_t)(size_t)((__attribute__((address_space(3))) char*)lds_base));
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(m0), "v"(voff), "s"(r) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(m0), "v"(voff), "s"(r), "s"(soff) : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const i32x4& r, char* lds_base, uint32_t voff) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(
@@ -296,28 +252,26 @@ __device__ __forceinline__ void dma4(const i32x4& r, char* lds_base, uint32_t vo
 // all of this wave's global->LDS loads have landed
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Per-lane byte offsets for loading a [ROWS][D] bf16 tile whose rows are
-// `ts_bytes` apart in global memory into the swizzled LDS layout with 16-byte
-// direct loads.  Wave w fills rows [ROWS/4*w, ROWS/4*(w+1)); its i-th load
-// covers 1024 contiguous LDS bytes, i.e. rows_per_load = 1024 / (2D) whole
-// rows, and lane l lands on chunk position l % (D/8) of row l / (D/8), which
-// holds logical chunk position ^ swz(row).
+// Loads a [64][D] bf16 tile whose rows are ts elements apart in global
+// memory into the column-group LDS layout with 16-byte direct loads.  One load
+// fills 1024 contiguous LDS bytes = 16 rows of one column group: lane l takes
+// row l / 4 of the 16 and chunk position l % 4, i.e. logical chunk
+// (l % 4) ^ ((l >> 4) & 3).  Wave w fills rows 16w..16w+15 of every column
+// group, so one per-lane offset serves all of its loads and the column group
+// goes into the scalar offset.  Rows at or past valid_rows lie at or past the
+// end of the buffer range whatever the scalar offset (< 2D bytes < one row),
+// so they read as zero.
 template <int D, int ROWS>
 struct TileDma {
-  static constexpr int ROWB = D * 2;
-  static constexpr int CPR = D / 8;              // chunks per row
-  static constexpr int RPL = 1024 / ROWB;        // rows per load
-  static constexpr int NL = ROWS / 4 / RPL;      // loads per wave
-  uint32_t voff[NL];
-  int row0;                                       // first row of this wave
+  static_assert(ROWS == 64 && D % 32 == 0, "tile shape");
+  static constexpr int NG = D / 32;           // column groups
+  uint32_t voff;
+  int w;
   __device__ __forceinline__ void init(int wid, int lane, int64_t ts_elems) {
-    row0 = wid * (ROWS / 4);
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int r = row0 + i * RPL + lane / CPR;
-      const int c = (lane % CPR) ^ swz<D>(r);
-      voff[i] = (uint32_t)(r * ts_elems * 2 + c * 16);
-    }
+    w = wid;
+    const int r = 16 * wid + (lane >> 2);
+    const int q = (lane & 3) ^ ((lane >> 4) & 3);
+    voff = (uint32_t)(r * ts_elems * 2 + q * 16);
   }
   // rows [row_base, row_base + ROWS) of a tensor (base pointer of row 0 of the
   // head), valid_rows of them in bounds
@@ -327,7 +281,8 @@ struct TileDma {
     const int vr = valid_rows < 0 ? 0 : (valid_rows > ROWS ? ROWS : valid_rows);
     const i32x4 r = make_rsrc(b, (uint32_t)(vr * ts_elems * 2));
 #pragma unroll
-    for (int i = 0; i < NL; ++i) dma16(r, lds_tile + (row0 + i * RPL) * ROWB, voff[i]);
+    for (int g = 0; g < NG; ++g)
+      dma16(r, lds_tile + g * group_bytes<ROWS>() + 16 * w * 64, voff, 64u * g);
   }
 };
 
