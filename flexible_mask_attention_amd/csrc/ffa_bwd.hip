@@ -63,7 +63,7 @@ __global__ __launch_bounds__(NT) void ffa_bwd_pre_kernel(BwdArgs a) {
 // dK, dV: owner (kv head, BN_B-key block), 4 waves x 32 keys.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(NT, 2) void ffa_bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void ffa_bwd_dkdv_kernel(BwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int TILE_B = BM_B * D * 2;          // bytes of one Q or dO tile
   constexpr int STAGE_B = 2 * TILE_B + 2 * BM_B * 4;
@@ -78,8 +78,9 @@ __global__ __launch_bounds__(NT, 2) void ffa_bwd_dkdv_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h32 = lane >> 5, t16 = lane & 15, g16 = lane >> 4;
-  const int kvh = blockIdx.x % a.Hkv;
-  const int n = mv.sched_b[blockIdx.x / a.Hkv];
+  int item, kvh;
+  xcd_map(blockIdx.x, a.Hkv, item, kvh);
+  const int n = mv.sched_b[item];
   const int key = n * BN_B + wid * 32 + l32;
   const bool kok = key < a.Tk;
   const int G = a.Hq / a.Hkv;
@@ -273,7 +274,7 @@ __global__ __launch_bounds__(NT, 2) void ffa_bwd_dkdv_kernel(BwdArgs a) {
 // dQ: owner (query head, BM_F-row block), 4 waves x 32 rows, q2k tiles.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(NT, 2) void ffa_bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void ffa_bwd_dq_kernel(BwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int TILE_B = BN_F * D * 2;
   constexpr int STAGE_B = 2 * TILE_B;
@@ -288,8 +289,9 @@ __global__ __launch_bounds__(NT, 2) void ffa_bwd_dq_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h32 = lane >> 5, t16 = lane & 15, g16 = lane >> 4;
-  const int head = blockIdx.x % a.Hq;
-  const int m = mv.sched_f[blockIdx.x / a.Hq];
+  int item, head;
+  xcd_map(blockIdx.x, a.Hq, item, head);
+  const int m = mv.sched_f[item];
   const int kvh = head / (a.Hq / a.Hkv);
   const int qrow = m * BM_F + wid * 32 + l32;
   const bool qok = qrow < a.Tq;

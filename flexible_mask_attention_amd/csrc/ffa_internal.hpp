@@ -236,34 +236,42 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t num_bytes)
 // lds_base + 16*l (4*l); the global address is base + voff + soff, soff being
 // wave-uniform.  Issued as inline assembly so that the compiler does not make
 // later LDS reads of the *other* buffer wait for these loads; the caller
-// waits explicitly (wait_dma) before the barrier that publishes them.
+// waits explicitly (wait_dma) before the barrier that publishes them.  m0 is
+// a register the compiler reserves and would not honour as a clobber; no
+// generated code of these kernels keeps a value in m0 across the statements.
 __device__ __forceinline__ void dma16(const i32x4& r, char* lds_base, uint32_t voff, uint32_t soff) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(
       (uint32_t)(size_t)((__attribute__((address_space(3))) char*)lds_base));
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :: "s"(m0), "v"(voff), "s"(r), "s"(soff) : "memory", "m0");
+               :: "s"(m0), "v"(voff), "s"(r), "s"(soff) : "memory");
 }
 __device__ __forceinline__ void dma4(const i32x4& r, char* lds_base, uint32_t voff) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(
       (uint32_t)(size_t)((__attribute__((address_space(3))) char*)lds_base));
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-               :: "s"(m0), "v"(voff), "s"(r) : "memory", "m0");
+               :: "s"(m0), "v"(voff), "s"(r) : "memory");
 }
 // all of this wave's global->LDS loads have landed
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// all but the N most recently issued of this wave's global->LDS loads have landed
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
 
-// Loads a [64][D] bf16 tile whose rows are ts elements apart in global
-// memory into the column-group LDS layout with 16-byte direct loads.  One load
-// fills 1024 contiguous LDS bytes = 16 rows of one column group: lane l takes
-// row l / 4 of the 16 and chunk position l % 4, i.e. logical chunk
-// (l % 4) ^ ((l >> 4) & 3).  Wave w fills rows 16w..16w+15 of every column
-// group, so one per-lane offset serves all of its loads and the column group
-// goes into the scalar offset.  Rows at or past valid_rows lie at or past the
-// end of the buffer range whatever the scalar offset (< 2D bytes < one row),
-// so they read as zero.
+// Loads a [ROWS][D] bf16 tile whose rows are ts elements apart in global
+// memory into the column-group LDS layout with 16-byte direct loads, using
+// ROWS / 16 waves.  One load fills 1024 contiguous LDS bytes = 16 rows of one
+// column group: lane l takes row l / 4 of the 16 and chunk position l % 4,
+// i.e. logical chunk (l % 4) ^ ((l >> 4) & 3).  Wave w fills rows
+// 16w..16w+15 of every column group, so one per-lane offset serves all of its
+// loads and the column group goes into the scalar offset.  Rows at or past
+// valid_rows lie at or past the end of the buffer range whatever the scalar
+// offset (< 2D bytes < one row), so they read as zero.
 template <int D, int ROWS>
 struct TileDma {
-  static_assert(ROWS == 64 && D % 32 == 0, "tile shape");
+  static_assert(ROWS % 16 == 0 && D % 32 == 0, "tile shape");
   static constexpr int NG = D / 32;           // column groups
   uint32_t voff;
   int w;
@@ -285,6 +293,24 @@ struct TileDma {
       dma16(r, lds_tile + g * group_bytes<ROWS>() + 16 * w * 64, voff, 64u * g);
   }
 };
+
+// Work items are (schedule position, head) pairs, nitems * H blocks in all.
+// Blocks are dispatched round-robin over the 8 XCDs (block b on XCD b % 8),
+// each with its own L2.  When H is a multiple of 8, XCD x is given the heads
+// [x H/8, (x+1) H/8) and takes their items in schedule order (heaviest
+// first), head-minor: consecutive blocks on one XCD are the heads of one
+// item, which share key/value (or query) tiles through that XCD's L2, and
+// every XCD receives the same amount of work.
+__device__ __forceinline__ void xcd_map(int bid, int H, int& item, int& head) {
+  if (H % 8 == 0) {
+    const int hx = H / 8, x = bid & 7, j = bid >> 3;
+    item = j / hx;
+    head = x * hx + j % hx;
+  } else {
+    item = bid / H;
+    head = bid % H;
+  }
+}
 
 __device__ __forceinline__ float wave_swap_max(float x) {
   auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
