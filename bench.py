@@ -13,6 +13,7 @@ Default workload: 16384-token varlen-causal GQA (Hq 32, Hkv 8, d 128), lengths
 U[256, 4096] trimmed to the total, seed 2.  Prints one JSON line.
 """
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -100,6 +101,69 @@ def phase_times(cases, reps):
     return {n: tot[n] / reps for n in names}
 
 
+def kernel_source_digest():
+    """sha256 over the HIP sources; recorded hardware counters are only used
+    while the kernels they were taken on are unchanged."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "flexible_mask_attention_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from profiles/traffic.json: FETCH_SIZE
+    and WRITE_SIZE (KiB per dispatch, rocprofv3 --pmc), each scaled by the
+    ratio of known bytes to what the same counter reads for a plain device
+    copy.  None when no record matches this kernel, workload and source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_sha256") != kernel_source_digest():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    if k is None or rec.get("workload") != workload:
+        return None
+    cal = rec["copy_calibration"]
+    f_fetch = cal["bytes"] / (cal["FETCH_SIZE_KiB"] * 1024.0)
+    f_write = cal["bytes"] / (cal["WRITE_SIZE_KiB"] * 1024.0)
+    return int(round(k["FETCH_SIZE_KiB"] * 1024.0 * f_fetch + k["WRITE_SIZE_KiB"] * 1024.0 * f_write))
+
+
+def profile_phase(cases, phase, reps):
+    """Launch one phase `reps` times (for hardware-counter runs under
+    rocprofv3 --pmc).  `copy` is the calibration kernel: a plain device copy
+    of 1 GiB, whose true HBM traffic is 1 GiB read + 1 GiB written."""
+    for cs in cases:
+        cs.step()
+    torch.cuda.synchronize()
+    if phase == "copy":
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(reps):
+            dst.copy_(src)
+    else:
+        for _ in range(reps):
+            for cs in cases:
+                if phase == "meta":
+                    cs.build_meta()
+                elif phase == "fwd":
+                    cs.fwd()
+                elif phase == "bwd_dkdv":
+                    cs.bwd(ffa.BWD_DKDV)
+                elif phase == "bwd_dq":
+                    cs.bwd(ffa.BWD_DQ)
+                else:
+                    raise SystemExit(f"unknown phase {phase}")
+    torch.cuda.synchronize()
+    log(f"profiled phase {phase}: {reps} launch(es) per call")
+
+
 def cpu_baseline(call, seed, area, min_seconds=10.0):
     """The fp64 oracle, untuned, timed on the host cores: forward + backward of
     the whole workload (all heads, full mask), repeated until at least
@@ -129,6 +193,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2, help="1..5 (see workloads.py)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-phase", default=None,
+                    help="meta|fwd|bwd_dkdv|bwd_dq|copy: only launch that phase --reps times "
+                         "(for hardware-counter runs); prints no JSON")
+    ap.add_argument("--reps", type=int, default=3)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         log("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -142,6 +210,9 @@ def main():
     areas = [cs.meta.area() for cs in cases]
     for cs in cases:
         assert cs.meta.status() == 0
+    if args.profile_phase:
+        profile_phase(cases, args.profile_phase, args.reps)
+        return
     f_fwd = sum(4.0 * cs.c.d * a * cs.c.Hq for cs, a in zip(cases, areas))
     f_bwd = 2.5 * f_fwd
 
@@ -173,7 +244,8 @@ def main():
     dom = max(("fwd", "bwd_dkdv", "bwd_dq"), key=lambda n: ph[n])
     achieved = kernels[dom]["tflops"]
     roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": recorded_traffic(dom, W.name), "traffic_unit": "HBM bytes per launch"}
 
     value = (f_fwd + f_bwd) / step_s / 1e12
     c0 = W.calls[0]

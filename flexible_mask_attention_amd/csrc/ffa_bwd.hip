@@ -130,11 +130,16 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     dvacc[i] = f32x16{};
   }
 
+  // Step u covers query head kvh*G + u % G of list entry nT - 1 - u / G: the
+  // lists (Partial, then Full, ascending) are walked backwards and the heads
+  // sharing this key head are interleaved, so every key block of a causal
+  // sequence starts at the sequence's last query tile and the blocks resident
+  // on one XCD move through the same Q / dO tiles at about the same time.
   const int total = G * nT;
   auto tile_of = [&](int t) { return t < nP ? pidx[t] : fidx[t - nP]; };
   auto issue = [&](int u, int stage) {
-    const int hq = kvh * G + u / nT;
-    const int m = tile_of(u % nT);
+    const int hq = kvh * G + u % G;
+    const int m = tile_of(nT - 1 - u / G);
     char* st = smem + stage * STAGE_B;
     const int vr = a.Tq - m * BM_B;
     dq_dma.load(a.q + (int64_t)hq * a.q_hs, a.q_ts, m * BM_B, vr, st);
@@ -150,7 +155,7 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
 
   auto tile = [&](auto stage_c, int u) {
     constexpr int stage = decltype(stage_c)::value;
-    const int t = u % nT;
+    const int t = nT - 1 - u / G;
     const bool masked = t < nP;
     const int m = tile_of(t);
     if (u + 1 < total) issue(u + 1, stage ^ 1);
