@@ -27,8 +27,10 @@ META_ERR_BOUNDS, META_ERR_TYPE, META_ERR_OVERLAP, META_ERR_CAPACITY = 1, 2, 4, 8
 EXPORTED = (
     "ffa_block_meta_workspace_size", "ffa_build_block_meta", "ffa_block_meta_view", "ffa_fwd",
     "ffa_bwd_workspace_size", "ffa_bwd", "ffa_bwd_phases", "ffa_status_string", "ffa_abi_version",
+    "ffa_fwd_ex", "ffa_bwd_ex",
 )
 BWD_PRE, BWD_DKDV, BWD_DQ, BWD_ALL = 1, 2, 4, 7
+ACCUMULATE = 1                  # FFA_ACCUMULATE flag of ffa_fwd_ex / ffa_bwd_ex
 
 
 class FFAError(RuntimeError):
@@ -88,6 +90,10 @@ def lib() -> ctypes.CDLL:
     L.ffa_bwd.restype = st
     L.ffa_bwd_phases.argtypes = L.ffa_bwd.argtypes[:-1] + [i32, vp]
     L.ffa_bwd_phases.restype = st
+    L.ffa_fwd_ex.argtypes = L.ffa_fwd.argtypes[:-1] + [ctypes.c_uint32, vp]
+    L.ffa_fwd_ex.restype = st
+    L.ffa_bwd_ex.argtypes = L.ffa_bwd.argtypes[:-1] + [i32, ctypes.c_uint32, vp]
+    L.ffa_bwd_ex.restype = st
     L.ffa_status_string.argtypes = [st]
     L.ffa_status_string.restype = ctypes.c_char_p
     L.ffa_abi_version.argtypes = []
@@ -224,8 +230,12 @@ def _shape(q, k, scale) -> Shape:
 
 
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, meta: BlockMeta, scale: float = None,
-        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, stream=None):
-    """Forward.  q [Tq,Hq,d], k/v [Tk,Hkv,d] bf16 -> (o [Tq,Hq,d] bf16, lse [Hq,Tq] fp32)."""
+        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, stream=None,
+        accumulate: bool = False):
+    """Forward.  q [Tq,Hq,d], k/v [Tk,Hkv,d] bf16 -> (o [Tq,Hq,d] bf16, lse [Hq,Tq] fp32).
+    ``accumulate``: merge into the (out, lse) given (ffa_fwd_ex with FFA_ACCUMULATE)."""
+    if accumulate and (out is None or lse is None):
+        raise FFAError("accumulate needs the previous out and lse")
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _check_thd(t, n)
     sh = _shape(q, k, scale)
@@ -233,8 +243,9 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, meta: BlockMeta, scal
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     if lse is None:
         lse = torch.empty(q.shape[1], q.shape[0], dtype=torch.float32, device=q.device)
-    _check(lib().ffa_fwd(ctypes.byref(sh), _tin(q), _tin(k), _tin(v), meta.ptr, _tout(out),
-                         lse.data_ptr(), _stream(stream)), "ffa_fwd")
+    _check(lib().ffa_fwd_ex(ctypes.byref(sh), _tin(q), _tin(k), _tin(v), meta.ptr, _tout(out),
+                            lse.data_ptr(), ACCUMULATE if accumulate else 0, _stream(stream)),
+           "ffa_fwd_ex")
     return out, lse
 
 
@@ -246,9 +257,13 @@ def bwd_workspace_size(q, k, scale=None) -> int:
 
 
 def bwd(q, k, v, o, lse, do, meta: BlockMeta, scale: float = None, dq=None, dk=None, dv=None,
-        workspace: Optional[torch.Tensor] = None, stream=None, phases: int = BWD_ALL):
+        workspace: Optional[torch.Tensor] = None, stream=None, phases: int = BWD_ALL,
+        accumulate: bool = False):
     """Backward -> (dq, dk, dv), bf16, same shapes as q, k, v.  ``phases``
-    selects a subset of the backward kernels (BWD_PRE | BWD_DKDV | BWD_DQ)."""
+    selects a subset of the backward kernels (BWD_PRE | BWD_DKDV | BWD_DQ);
+    ``accumulate`` adds to the dq, dk, dv given (ffa_bwd_ex with FFA_ACCUMULATE)."""
+    if accumulate and (dq is None or dk is None or dv is None):
+        raise FFAError("accumulate needs the dq, dk, dv to add to")
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
         _check_thd(t, n)
     sh = _shape(q, k, scale)
@@ -258,9 +273,10 @@ def bwd(q, k, v, o, lse, do, meta: BlockMeta, scale: float = None, dq=None, dk=N
     need = bwd_workspace_size(q, k, scale)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    _check(lib().ffa_bwd_phases(ctypes.byref(sh), _tin(q), _tin(k), _tin(v), _tin(o), lse.data_ptr(),
-                                _tin(do), meta.ptr, _tout(dq), _tout(dk), _tout(dv), workspace.data_ptr(),
-                                workspace.numel(), int(phases), _stream(stream)), "ffa_bwd_phases")
+    _check(lib().ffa_bwd_ex(ctypes.byref(sh), _tin(q), _tin(k), _tin(v), _tin(o), lse.data_ptr(),
+                            _tin(do), meta.ptr, _tout(dq), _tout(dk), _tout(dv), workspace.data_ptr(),
+                            workspace.numel(), int(phases), ACCUMULATE if accumulate else 0,
+                            _stream(stream)), "ffa_bwd_ex")
     return dq, dk, dv
 
 
@@ -284,6 +300,6 @@ def ffa_attention(q, k, v, meta: BlockMeta, scale: float = None) -> torch.Tensor
     return FFAFunction.apply(q, k, v, meta, scale)
 
 
-__all__ = ["BWD_PRE", "BWD_DKDV", "BWD_DQ", "BWD_ALL", "build_meta", "fwd", "bwd", "ffa_attention", "FFAFunction", "BlockMeta", "lib",
+__all__ = ["BWD_PRE", "BWD_DKDV", "BWD_DQ", "BWD_ALL", "ACCUMULATE", "build_meta", "fwd", "bwd", "ffa_attention", "FFAFunction", "BlockMeta", "lib",
            "meta_workspace_size", "bwd_workspace_size", "FFAError", "FULL", "CAUSAL", "INV_CAUSAL",
            "BI_CAUSAL", "EXPORTED"]

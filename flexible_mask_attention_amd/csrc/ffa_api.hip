@@ -130,6 +130,13 @@ FFA_API ffa_status ffa_block_meta_view(const void* d_meta, int32_t num_slices, i
 FFA_API ffa_status ffa_fwd(const ffa_shape* shape, ffa_tensor_in q, ffa_tensor_in k,
                            ffa_tensor_in v, const void* d_meta, ffa_tensor_out o, float* lse,
                            void* stream) {
+  return ffa_fwd_ex(shape, q, k, v, d_meta, o, lse, 0u, stream);
+}
+
+FFA_API ffa_status ffa_fwd_ex(const ffa_shape* shape, ffa_tensor_in q, ffa_tensor_in k,
+                              ffa_tensor_in v, const void* d_meta, ffa_tensor_out o, float* lse,
+                              uint32_t flags, void* stream) {
+  if (flags & ~FFA_ACCUMULATE) return FFA_ERR_INVALID_ARGUMENT;
   ffa_status st = check_shape(shape);
   if (st != FFA_OK) return st;
   const int D = shape->head_dim, Tq = shape->seqlen_q, Tk = shape->seqlen_k;
@@ -164,6 +171,7 @@ FFA_API ffa_status ffa_fwd(const ffa_shape* shape, ffa_tensor_in q, ffa_tensor_i
   a.Hkv = Hkv;
   a.scale = shape->softmax_scale;
   a.scale_log2 = shape->softmax_scale * LOG2E;
+  a.flags = flags;
   hipError_t e = launch_fwd(a, D, L.nq_f, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? FFA_OK : FFA_ERR_HIP;
 }
@@ -190,7 +198,17 @@ FFA_API ffa_status ffa_bwd_phases(const ffa_shape* shape, ffa_tensor_in q, ffa_t
                                   ffa_tensor_in dout, const void* d_meta, ffa_tensor_out dq,
                                   ffa_tensor_out dk, ffa_tensor_out dv, void* d_ws,
                                   size_t ws_bytes, int32_t phases, void* stream) {
+  return ffa_bwd_ex(shape, q, k, v, o, lse, dout, d_meta, dq, dk, dv, d_ws, ws_bytes, phases, 0u,
+                    stream);
+}
+
+FFA_API ffa_status ffa_bwd_ex(const ffa_shape* shape, ffa_tensor_in q, ffa_tensor_in k,
+                              ffa_tensor_in v, ffa_tensor_in o, const float* lse,
+                              ffa_tensor_in dout, const void* d_meta, ffa_tensor_out dq,
+                              ffa_tensor_out dk, ffa_tensor_out dv, void* d_ws, size_t ws_bytes,
+                              int32_t phases, uint32_t flags, void* stream) {
   if (phases & ~FFA_BWD_ALL) return FFA_ERR_INVALID_ARGUMENT;
+  if (flags & ~FFA_ACCUMULATE) return FFA_ERR_INVALID_ARGUMENT;
   ffa_status st = check_shape(shape);
   if (st != FFA_OK) return st;
   const int D = shape->head_dim, Tq = shape->seqlen_q, Tk = shape->seqlen_k;
@@ -248,6 +266,7 @@ FFA_API ffa_status ffa_bwd_phases(const ffa_shape* shape, ffa_tensor_in q, ffa_t
   a.Hkv = Hkv;
   a.scale = shape->softmax_scale;
   a.scale_log2 = shape->softmax_scale * LOG2E;
+  a.flags = flags;
   hipError_t e = launch_bwd(a, D, L.nq_f, L.nk_b, phases, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? FFA_OK : FFA_ERR_HIP;
 }

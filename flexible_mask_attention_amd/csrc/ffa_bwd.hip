@@ -257,20 +257,29 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   }
 
   if (kok) {
+    // FFA_ACCUMULATE: add to what dk / dv hold (fp32 sum, one rounding)
+    const bool acc = (a.flags & FFA_ACCUMULATE) != 0;
     __bf16* kp = a.dk + (int64_t)key * a.dk_ts + (int64_t)kvh * a.dk_hs;
     __bf16* vp = a.dv + (int64_t)key * a.dv_ts + (int64_t)kvh * a.dv_hs;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
+        bf16x4* dk4 = reinterpret_cast<bf16x4*>(kp + 32 * mb + 8 * j + 4 * h32);
+        bf16x4* dv4 = reinterpret_cast<bf16x4*>(vp + 32 * mb + 8 * j + 4 * h32);
+        bf16x4 ok = bf16x4{}, ov = bf16x4{};
+        if (acc) {
+          ok = *dk4;
+          ov = *dv4;
+        }
         bf16x4 wk, wv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          wk[i] = static_cast<__bf16>(dkacc[mb][4 * j + i] * a.scale);
-          wv[i] = static_cast<__bf16>(dvacc[mb][4 * j + i]);
+          wk[i] = static_cast<__bf16>(dkacc[mb][4 * j + i] * a.scale + static_cast<float>(ok[i]));
+          wv[i] = static_cast<__bf16>(dvacc[mb][4 * j + i] + static_cast<float>(ov[i]));
         }
-        *reinterpret_cast<bf16x4*>(kp + 32 * mb + 8 * j + 4 * h32) = wk;
-        *reinterpret_cast<bf16x4*>(vp + 32 * mb + 8 * j + 4 * h32) = wv;
+        *dk4 = wk;
+        *dv4 = wv;
       }
   }
 }
@@ -440,15 +449,21 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   }
 
   if (qok) {
+    // FFA_ACCUMULATE: add to what dq holds (fp32 sum, one rounding)
+    const bool acc = (a.flags & FFA_ACCUMULATE) != 0;
     __bf16* qp = a.dq + (int64_t)qrow * a.dq_ts + (int64_t)head * a.dq_hs;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
+        bf16x4* dst = reinterpret_cast<bf16x4*>(qp + 32 * mb + 8 * j + 4 * h32);
+        bf16x4 old = bf16x4{};
+        if (acc) old = *dst;
         bf16x4 w;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = static_cast<__bf16>(dqacc[mb][4 * j + i] * a.scale);
-        *reinterpret_cast<bf16x4*>(qp + 32 * mb + 8 * j + 4 * h32) = w;
+        for (int i = 0; i < 4; ++i)
+          w[i] = static_cast<__bf16>(dqacc[mb][4 * j + i] * a.scale + static_cast<float>(old[i]));
+        *dst = w;
       }
   }
 }

@@ -242,25 +242,50 @@ void ffa_fwd_kernel(FwdArgs a) {
     if (u + 1 < nU) stage_fn(std::integral_constant<int, 1>{}, u + 1);
   }
 
-  // epilogue: O = O^T / l, LSE = m*scale + ln l (natural log)
+  // epilogue: O = O^T / l, LSE = m*scale + ln l (natural log).  With
+  // FFA_ACCUMULATE the row is merged into the (O_1, LSE_1) already stored:
+  // LSE = ln(e^LSE_1 + e^LSE_2), O = e^(LSE_1-LSE) O_1 + e^(LSE_2-LSE) O_2;
+  // a row without valid keys in this call keeps its stored values.
+  const bool acc = (a.flags & FFA_ACCUMULATE) != 0;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int qrow = row0 + 32 * qb;
     const float l_tot = wave_swap_sum(l_run[qb]);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (qrow < a.Tq) {
-      __bf16* op = a.o + (int64_t)qrow * a.o_ts + (int64_t)head * a.o_hs;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          bf16x4 w;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) w[i] = static_cast<__bf16>(oacc[qb][mb][4 * j + i] * inv);
-          *reinterpret_cast<bf16x4*>(op + 32 * mb + 8 * j + 4 * h32) = w;
+      float lse_new = l_tot > 0.f ? m_run[qb] * a.scale + logf(l_tot) : -INFINITY;
+      float w_new = l_tot > 0.f ? 1.f / l_tot : 0.f, w_old = 0.f;
+      bool write = true;
+      float* lp = a.lse + (int64_t)head * a.Tq + qrow;
+      if (acc) {
+        const float lse_old = *lp;
+        if (lse_new == -INFINITY) {
+          write = false;
+        } else if (lse_old != -INFINITY) {
+          const float mx = fmaxf(lse_old, lse_new);
+          const float e1 = expf(lse_old - mx), e2 = expf(lse_new - mx);
+          const float den = e1 + e2;
+          lse_new = mx + logf(den);
+          w_old = e1 / den;
+          w_new *= e2 / den;
         }
-      if (h32 == 0)
-        a.lse[(int64_t)head * a.Tq + qrow] = l_tot > 0.f ? m_run[qb] * a.scale + logf(l_tot) : -INFINITY;
+      }
+      if (write) {
+        __bf16* op = a.o + (int64_t)qrow * a.o_ts + (int64_t)head * a.o_hs;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            bf16x4* dst = reinterpret_cast<bf16x4*>(op + 32 * mb + 8 * j + 4 * h32);
+            bf16x4 old = bf16x4{};
+            if (w_old != 0.f) old = *dst;
+            bf16x4 w;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              w[i] = static_cast<__bf16>(oacc[qb][mb][4 * j + i] * w_new + static_cast<float>(old[i]) * w_old);
+            *dst = w;
+          }
+        if (h32 == 0) *lp = lse_new;
+      }
     }
   }
 }

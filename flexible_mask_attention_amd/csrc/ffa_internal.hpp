@@ -341,6 +341,7 @@ struct FwdArgs {
   int32_t Tq, Tk, Hq, Hkv;
   float scale_log2;   // softmax_scale * log2(e)
   float scale;
+  uint32_t flags;     // FFA_ACCUMULATE: merge into the (o, lse) already in the buffers
 };
 hipError_t launch_fwd(const FwdArgs& a, int head_dim, int nq_f, hipStream_t stream);
 
@@ -362,6 +363,7 @@ struct BwdArgs {
   int32_t Tq, Tk, Hq, Hkv;
   float scale_log2;
   float scale;
+  uint32_t flags;     // FFA_ACCUMULATE: add to the dq / dk / dv already in the buffers
 };
 hipError_t launch_bwd(const BwdArgs& a, int head_dim, int nq_f, int nk_b, int phases,
                       hipStream_t stream);

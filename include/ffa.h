@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define FFA_ABI_VERSION 1
+#define FFA_ABI_VERSION 2
 
 #if defined(__GNUC__)
 #define FFA_API __attribute__((visibility("default")))
@@ -197,6 +197,38 @@ FFA_API ffa_status ffa_bwd_phases(const ffa_shape* shape, ffa_tensor_in q, ffa_t
                                   ffa_tensor_in dout, const void* d_meta, ffa_tensor_out dq,
                                   ffa_tensor_out dk, ffa_tensor_out dv, void* d_ws,
                                   size_t ws_bytes, int32_t phases, void* stream);
+
+/* Flags of ffa_fwd_ex and ffa_bwd_ex. */
+#define FFA_ACCUMULATE 1u  /* merge into / add to the results already in the output buffers */
+
+/* ffa_fwd with flags; flags = 0 is ffa_fwd.  FFA_ACCUMULATE is the partial-result merge that
+ * lets one attention be computed in several calls whose valid (query, key) sets are
+ * disjoint, e.g. one call per stage of key / value ranges arriving from other GPUs
+ * (MagiAttention blog deep-dive, section "通信与重叠", Fig. 13: the forward runs stage by
+ * stage; section "Flex-Flash-Attention 与 AttnSlice", Fig. 5: partial results are merged).
+ * o and lse must then hold a previous result (O_1, LSE_1) of the same queries, LSE_1 = -inf
+ * for rows that had no valid key (their O_1 is not read).  This call's result (O_2, LSE_2)
+ * is merged into them row by row with the log-sum-exp identity
+ *   LSE = ln(e^LSE_1 + e^LSE_2),  O = e^(LSE_1 - LSE) O_1 + e^(LSE_2 - LSE) O_2
+ * (fp32, O rounded to bf16 once per call); rows with no valid key in this call keep their
+ * stored O and LSE.  Unknown flag bits give FFA_ERR_INVALID_ARGUMENT. */
+FFA_API ffa_status ffa_fwd_ex(const ffa_shape* shape, ffa_tensor_in q, ffa_tensor_in k,
+                              ffa_tensor_in v, const void* d_meta, ffa_tensor_out o, float* lse,
+                              uint32_t flags, void* stream);
+
+/* ffa_bwd_phases with flags; flags = 0 is ffa_bwd_phases.  With FFA_ACCUMULATE the DQ phase
+ * adds its result to what dq holds and the DKDV phase to what dk and dv hold (fp32 sum,
+ * rounded to bf16 once per call), the backward counterpart of the merge above (blog
+ * deep-dive, section "通信与重叠", Fig. 13: partial dKV reduced stage by stage).  When an
+ * attention is split into calls with disjoint valid sets, passing every call the merged o and
+ * lse of the whole forward makes each call produce exactly its share of dQ, dK and dV, so the
+ * accumulated buffers hold the gradients of the whole.  Unknown flag bits give
+ * FFA_ERR_INVALID_ARGUMENT. */
+FFA_API ffa_status ffa_bwd_ex(const ffa_shape* shape, ffa_tensor_in q, ffa_tensor_in k,
+                              ffa_tensor_in v, ffa_tensor_in o, const float* lse,
+                              ffa_tensor_in dout, const void* d_meta, ffa_tensor_out dq,
+                              ffa_tensor_out dk, ffa_tensor_out dv, void* d_ws, size_t ws_bytes,
+                              int32_t phases, uint32_t flags, void* stream);
 
 /* Static description of a status code. */
 FFA_API const char* ffa_status_string(ffa_status status);

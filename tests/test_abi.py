@@ -23,7 +23,7 @@ def declared_symbols():
 
 def test_exports_every_declared_symbol():
     names = declared_symbols()
-    assert len(names) == 9 and set(names) == set(ffa.EXPORTED)
+    assert len(names) == 11 and set(names) == set(ffa.EXPORTED)
     L = ffa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol():
 
 def test_abi_version_and_strings():
     L = ffa.lib()
-    assert L.ffa_abi_version() == 1
+    assert L.ffa_abi_version() == 2
     for code in range(5):
         assert len(L.ffa_status_string(code)) > 0
 
@@ -78,6 +78,13 @@ def test_host_validation_returns_before_enqueue():
                      None, ws.value, None) == 1
     assert L.ffa_bwd_phases(P(_shape()), good, good, good, good, lse, good, meta, goodo, goodo, goodo,
                             0x100000, ws.value, 8, None) == 1
+    # unknown flag bits of the accumulate entry points
+    assert L.ffa_fwd_ex(P(_shape()), good, good, good, meta, goodo, lse, 2, None) == 1
+    assert L.ffa_fwd_ex(P(_shape(d=96)), good, good, good, meta, goodo, lse, 1, None) == 2
+    assert L.ffa_bwd_ex(P(_shape()), good, good, good, good, lse, good, meta, goodo, goodo, goodo,
+                        0x100000, ws.value, 7, 4, None) == 1
+    assert L.ffa_bwd_ex(P(_shape()), good, good, good, good, lse, good, meta, goodo, goodo, goodo,
+                        0x100000, ws.value - 1, 7, 1, None) == 3
     # metadata build: bad sizes, misaligned buffer, too-small buffer
     n = ctypes.c_size_t()
     assert L.ffa_block_meta_workspace_size(-1, 10, 10, 64, None, P(n)) == 1
