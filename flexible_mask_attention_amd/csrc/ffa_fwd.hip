@@ -7,17 +7,18 @@
 // create_block_mask / CSR tile lists of the documentation page ("FFA_FA4"
 // optimisations) so that only Partial tiles pay for per-element masking.
 //
-// Work item: (query head, 128-row query block), 2 waves, 64 query rows each
-// (two 32-row MFMA blocks).  The kernel computes S^T = K Q^T with
-// v_mfma_f32_32x32x16_bf16 so that each lane owns one query row per block:
-// its softmax statistics stay in registers and only one half-wave swap is
-// needed per row max.  The P^T accumulator registers feed the next MFMA
-// (O^T += V^T P^T) directly as its B operand; V^T comes from LDS through
-// ds_read_b64_tr_b16.  Every K or V operand read from LDS serves both row
-// blocks of the wave, which halves LDS traffic per MFMA compared with one
-// 32-row block per wave.  Each 64-key tile of the lists is streamed as two
-// 32-key stages through a double-buffered LDS ring; the loads for stage s+1
-// are issued before stage s is computed.
+// Work item: (query head, 128-row query block), 4 waves of 32 query rows.
+// The kernel computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 so that each
+// lane owns one query row: its softmax statistics stay in registers and only
+// one half-wave swap is needed per row max.  The P^T accumulator registers
+// feed the next MFMA (O^T += V^T P^T) directly as its B operand; V^T comes
+// from LDS through ds_read_b64_tr_b16.  Each 64-key tile of the lists is
+// streamed as two 32-key stages through a double-buffered LDS ring (32 KB per
+// workgroup at d = 128); the loads for stage s+1 are issued before stage s is
+// computed.  At under 170 VGPRs and 32 KB of LDS, three workgroups share a
+// CU, i.e. three waves per SIMD hide each other's LDS, exponent and MFMA
+// latencies (measured faster than two waves of two 32-row blocks each, which
+// halve the LDS reads per MFMA but need 253 VGPRs).
 #include <type_traits>
 
 #include "ffa_internal.hpp"
@@ -26,15 +27,15 @@ namespace ffa {
 
 namespace {
 
-constexpr int NW = 2;                 // waves per block
+constexpr int NW = 4;                 // waves per block
 constexpr int NT = 64 * NW;
 constexpr int RW = BM_F / NW;         // query rows per wave
 constexpr int QB = RW / 32;           // 32-row MFMA blocks per wave
 constexpr int SK = 32;                // keys per stage
-static_assert(QB == 2 && BN_F % SK == 0 && SK == 16 * NW, "forward tiling");
+static_assert(QB == 1 && BN_F % SK == 0 && 2 * SK == 16 * NW, "forward tiling");
 
 template <int D>
-__global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(NT, 3) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void ffa_fwd_kernel(FwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int TILE_B = SK * D * 2;            // bytes of one K or V stage tile
@@ -43,12 +44,6 @@ void ffa_fwd_kernel(FwdArgs a) {
   constexpr int KS = D / 16;                    // 16-wide d steps of S^T
   constexpr int GB = group_bytes<SK>();
   constexpr int HALVES = BN_F / SK;
-  // The last NQL 16-wide d steps of the second row block's Q operand live in
-  // LDS instead of registers (16 bytes per lane each, read once per stage):
-  // at d = 128 this keeps the kernel within 256 VGPRs, i.e. two waves per
-  // SIMD, without scratch spills.
-  constexpr int NQL = D == 128 ? 4 : 0;
-  constexpr int QREG = KS - NQL;
 
   const MetaView mv = meta_view(a.meta);
   const FFA_CONST MetaHeader* hd = mv.hdr;
@@ -85,15 +80,6 @@ void ffa_fwd_kernel(FwdArgs a) {
   }
 
   wait_vmem();
-  char* qlds = smem + 2 * STAGE_B + wid * (NQL * 1024) + lane * 16;
-#pragma unroll
-  for (int k = QREG; k < KS; ++k) {
-    u32x4 u;
-    __builtin_memcpy(&u, &qop[1][k], 16);
-    *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
-        (__attribute__((address_space(3))) char*)qlds + (k - QREG) * 1024) = u;
-  }
-
   // loop-invariant LDS read bases (stage, column group and chunk offsets are
   // immediates): the 128-bit K read of chunk 2k + h32 of key l32 is at
   // (k / 2) * GB + kaddr[k % 2], the transposed V read of keys 8j.. of column
@@ -105,18 +91,17 @@ void ffa_fwd_kernel(FwdArgs a) {
   for (int j = 0; j < 2; ++j)
     vaddr[j] = lds_pos(4 * h32 + (t16 >> 2) + 8 * j, 2 * (g16 & 1) + ((t16 >> 1) & 1)) + 8 * (t16 & 1);
 
-  TileDma<D, SK> dmk;
-  dmk.init(wid, lane, a.k_ts);
-  TileDma<D, SK> dmv;
-  dmv.init(wid, lane, a.v_ts);
+  // waves 0-1 load the K stage tile, waves 2-3 the V stage tile
+  TileDma<D, SK> dm;
+  dm.init(wid & 1, lane, wid < 2 ? a.k_ts : a.v_ts);
   const __bf16* kbase = a.k + (int64_t)kvh * a.k_hs;
   const __bf16* vbase = a.v + (int64_t)kvh * a.v_hs;
   auto tile_of = [&](int t) { return t < nP ? pidx[t] : fidx[t - nP]; };
   auto issue = [&](int u, int stage) {
     const int key0 = tile_of(u / HALVES) * BN_F + (u % HALVES) * SK;
     char* st = smem + stage * STAGE_B;
-    dmk.load(kbase, a.k_ts, key0, a.Tk - key0, st);
-    dmv.load(vbase, a.v_ts, key0, a.Tk - key0, st + TILE_B);
+    if (wid < 2) dm.load(kbase, a.k_ts, key0, a.Tk - key0, st);
+    else dm.load(vbase, a.v_ts, key0, a.Tk - key0, st + TILE_B);
   };
 
   f32x16 oacc[QB][MB];
@@ -142,7 +127,7 @@ void ffa_fwd_kernel(FwdArgs a) {
     const __attribute__((address_space(3))) char* lb =
         (const __attribute__((address_space(3))) char*)smem + stage * STAGE_B;
 
-    // S^T = K Q^T for both row blocks; each K read feeds two MFMAs
+    // S^T = K Q^T
     f32x16 sacc[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) sacc[qb] = f32x16{};
@@ -152,15 +137,6 @@ void ffa_fwd_kernel(FwdArgs a) {
       bf16x8 kop;
       __builtin_memcpy(&kop, &u4, 16);
       sacc[0] = mfma32(kop, qop[0][k], sacc[0]);
-      if (k < QREG) {
-        sacc[1] = mfma32(kop, qop[1][k], sacc[1]);
-      } else {
-        u32x4 uq = *(const __attribute__((address_space(3))) u32x4*)(
-            (const __attribute__((address_space(3))) char*)qlds + (k - QREG) * 1024);
-        bf16x8 qv;
-        __builtin_memcpy(&qv, &uq, 16);
-        sacc[1] = mfma32(kop, qv, sacc[1]);
-      }
     }
 
     if (masked) {
@@ -213,8 +189,7 @@ void ffa_fwd_kernel(FwdArgs a) {
       l_run[qb] += psum;
     }
 
-    // O^T += V^T P^T over the stage's two 16-key chunks; each V read feeds
-    // two MFMAs
+    // O^T += V^T P^T over the stage's two 16-key chunks
 #pragma unroll
     for (int cc = 0; cc < SK / 16; ++cc) {
 #pragma unroll
@@ -296,7 +271,7 @@ hipError_t launch_fwd(const FwdArgs& a, int head_dim, int nq_f, hipStream_t stre
   const int64_t grid = (int64_t)nq_f * a.Hq;
   if (grid == 0) return hipSuccess;
   if (head_dim == 128) {
-    const size_t lds = 2 * 2 * SK * 128 * 2 + NW * 4 * 1024;   // 40 KB: four blocks per CU
+    const size_t lds = 2 * 2 * SK * 128 * 2;
     ffa_fwd_kernel<128><<<dim3((unsigned)grid), NT, lds, stream>>>(a);
   } else {
     const size_t lds = 2 * 2 * SK * 64 * 2;
