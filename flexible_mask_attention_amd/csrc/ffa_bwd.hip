@@ -7,7 +7,7 @@
 // element has one owner and a fixed summation order, hence bitwise
 // reproducible results without atomics:
 //
-//   bwd_pre : D_i = dO_i . O_i                          (fp32, [Hq][Tq])
+//   bwd_pre : -D_i = -dO_i . O_i, LSE_i log2 e          (fp32, [Hq][Tq])
 //   dkdv    : owner (kv head, 128-key block); loops over the query heads that
 //             share the kv head and the k2q tiles of the block, in list order:
 //             S = Q K^T, P = exp(S - LSE) (masked on Partial tiles),
@@ -29,7 +29,8 @@ namespace {
 
 constexpr int NT = 256;
 
-// D_i = sum_c dO_ic O_ic, one group of D/8 lanes per (token, head)
+// -D_i = -sum_c dO_ic O_ic (stored negated: it seeds the dP accumulators) and
+// LSE_i log2 e, one group of D/8 lanes per (token, head)
 template <int D>
 __global__ __launch_bounds__(NT) void ffa_bwd_pre_kernel(BwdArgs a) {
   constexpr int G = D / 8;
@@ -53,7 +54,7 @@ __global__ __launch_bounds__(NT) void ffa_bwd_pre_kernel(BwdArgs a) {
 #pragma unroll
   for (int off = G / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, G);
   if (ok && part == 0) {
-    a.dvec[(int64_t)h * a.Tq + i] = acc;
+    a.dvec[(int64_t)h * a.Tq + i] = -acc;
     const float l = a.lse[(int64_t)h * a.Tq + i];
     a.lvec[(int64_t)h * a.Tq + i] = (l == -INFINITY) ? 0.f : l * LOG2E;
   }
@@ -184,8 +185,17 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     // one 32-row half at a time, so that only one S / dP pair is live
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      // S = Q K^T and dP = dO V^T; lane = key, registers = rows 32qb + 8(r/4) + 4*h32 + r%4
-      f32x16 sacc = f32x16{}, pacc = f32x16{};
+      // S = Q K^T and dP - D = dO V^T - D; lane = key, registers = rows
+      // 32qb + 8(r/4) + 4*h32 + r%4.  The dP accumulator starts at -D (four
+      // 128-bit LDS reads), which saves the subtraction in dS = P (dP - D).
+      f32x16 sacc = f32x16{}, pacc;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 nd = *(const __attribute__((address_space(3))) f32x4*)(
+            lb + laddr + (32 * qb + 8 * j) * 4 + BM_B * 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pacc[4 * j + i] = nd[i];
+      }
 #pragma unroll
       for (int k = 0; k < KS; ++k) {
         bf16x8 qa, ga;
@@ -206,15 +216,13 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
       // P = exp2(S c - LSE log2 e), dS = P (dP - D)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int ro = laddr + (32 * qb + 8 * j) * 4;
-        const f32x4 l4 = *(const __attribute__((address_space(3))) f32x4*)(lb + ro);
-        const f32x4 d4 = *(const __attribute__((address_space(3))) f32x4*)(lb + ro + BM_B * 4);
+        const f32x4 l4 = *(const __attribute__((address_space(3))) f32x4*)(lb + laddr + (32 * qb + 8 * j) * 4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 4 * j + i;
           const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -l4[i]));
           sacc[r] = pv;
-          pacc[r] = pv * (pacc[r] - d4[i]);
+          pacc[r] *= pv;
         }
       }
 
@@ -286,15 +294,37 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
 
 // ---------------------------------------------------------------------------
 // dQ: owner (query head, BM_F-row block), 4 waves x 32 rows, q2k tiles.
+//
+// Mirror of the forward: S^T = K Q^T and dP^T = V dO^T with one query row per
+// lane, dS^T = P^T (dP^T - D), dQ^T += K^T dS^T with K^T from transposed LDS
+// reads.  Each 64-key list tile streams as two 32-key stages through a
+// double-buffered LDS ring (32 KB); the last DQ_NQL 16-wide d steps of the Q
+// operand are parked in LDS (16 bytes per lane each, read once per stage) so
+// that the kernel stays within the registers of three waves per SIMD.
 // ---------------------------------------------------------------------------
+constexpr int DQ_SK = 32;                       // keys per stage
+
 template <int D>
-__global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void ffa_bwd_dq_kernel(BwdArgs a) {
+constexpr int dq_nql() { return D == 128 ? 4 : 0; }
+
+template <int D>
+constexpr size_t dq_lds_bytes() {
+  return 2 * 2 * DQ_SK * D * 2 + (size_t)(NT / 64) * dq_nql<D>() * 1024;
+}
+
+template <int D>
+__global__ __launch_bounds__(NT, 3) __attribute__((amdgpu_waves_per_eu(3, 3))) void ffa_bwd_dq_kernel(BwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  constexpr int TILE_B = BN_F * D * 2;
+  constexpr int SK = DQ_SK;
+  constexpr int TILE_B = SK * D * 2;            // one K or V stage tile
   constexpr int STAGE_B = 2 * TILE_B;
-  constexpr int KB = BN_F / 32;
   constexpr int MB = D / 32;
   constexpr int KS = D / 16;
+  constexpr int HALVES = BN_F / SK;
+  constexpr int NQL = dq_nql<D>();
+  constexpr int QREG = KS - NQL;
+  constexpr int GB = group_bytes<SK>();
+  static_assert(2 * SK == 16 * (NT / 64), "K and V stage tiles are loaded by half of the waves each");
 
   const MetaView mv = meta_view(a.meta);
   const FFA_CONST MetaHeader* hd = mv.hdr;
@@ -312,7 +342,7 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
 
   const int f0 = mv.qf_off[m], nF = mv.qf_off[m + 1] - f0;
   const int p0 = mv.qm_off[m], nP = mv.qm_off[m + 1] - p0;
-  const int nT = nP + nF;
+  const int nU = HALVES * (nP + nF);            // stages
   cint32_t* fidx = mv.var + hd->list_off[L_QF] + f0;
   cint32_t* pidx = mv.var + hd->list_off[L_QM] + p0;
   const int s0 = mv.qs_off[m], nS = mv.qs_off[m + 1] - s0;
@@ -330,14 +360,21 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
       __builtin_memcpy(&gop[k], &w, 16);
     }
   }
-  float l2 = 0.f, dval = 0.f;
+  float l2 = 0.f, ndval = 0.f;                   // LSE log2(e) and -D of this row
   if (qok) {
     l2 = a.lvec[(int64_t)head * a.Tq + qrow];
-    dval = a.dvec[(int64_t)head * a.Tq + qrow];
+    ndval = a.dvec[(int64_t)head * a.Tq + qrow];
   }
   wait_vmem();
+  char* qlds = smem + 2 * STAGE_B + wid * (NQL * 1024) + lane * 16;
+#pragma unroll
+  for (int k = QREG; k < KS; ++k) {
+    u32x4 u;
+    __builtin_memcpy(&u, &qop[k], 16);
+    *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
+        (__attribute__((address_space(3))) char*)qlds + (k - QREG) * 1024) = u;
+  }
 
-  constexpr int GB = group_bytes<BN_F>();
   int raddr[2], taddr[2];
 #pragma unroll
   for (int p = 0; p < 2; ++p) raddr[p] = lds_pos(l32, 2 * p + h32);
@@ -345,17 +382,17 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   for (int j = 0; j < 2; ++j)
     taddr[j] = lds_pos(4 * h32 + (t16 >> 2) + 8 * j, 2 * (g16 & 1) + ((t16 >> 1) & 1)) + 8 * (t16 & 1);
 
-  TileDma<D, BN_F> dmk, dmv;
-  dmk.init(wid, lane, a.k_ts);
-  dmv.init(wid, lane, a.v_ts);
+  // waves 0-1 load the K stage tile, waves 2-3 the V stage tile
+  TileDma<D, SK> dm;
+  dm.init(wid & 1, lane, wid < 2 ? a.k_ts : a.v_ts);
   const __bf16* kbase = a.k + (int64_t)kvh * a.k_hs;
   const __bf16* vbase = a.v + (int64_t)kvh * a.v_hs;
   auto tile_of = [&](int t) { return t < nP ? pidx[t] : fidx[t - nP]; };
-  auto issue = [&](int t, int stage) {
-    const int n = tile_of(t);
+  auto issue = [&](int u, int stage) {
+    const int key0 = tile_of(u / HALVES) * BN_F + (u % HALVES) * SK;
     char* st = smem + stage * STAGE_B;
-    dmk.load(kbase, a.k_ts, n * BN_F, a.Tk - n * BN_F, st);
-    dmv.load(vbase, a.v_ts, n * BN_F, a.Tk - n * BN_F, st + TILE_B);
+    if (wid < 2) dm.load(kbase, a.k_ts, key0, a.Tk - key0, st);
+    else dm.load(vbase, a.v_ts, key0, a.Tk - key0, st + TILE_B);
   };
 
   f32x16 dqacc[MB];
@@ -363,69 +400,64 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   for (int i = 0; i < MB; ++i) dqacc[i] = f32x16{};
   const float c = a.scale_log2;
 
-  auto tile = [&](auto stage_c, int t) {
+  auto stage_fn = [&](auto stage_c, int u) {
     constexpr int stage = decltype(stage_c)::value;
+    const int t = u / HALVES;
     const bool masked = t < nP;
-    const int n = tile_of(t);
-    if (t + 1 < nT) issue(t + 1, stage ^ 1);
+    const int key0 = tile_of(t) * BN_F + (u % HALVES) * SK;
+    if (u + 1 < nU) issue(u + 1, stage ^ 1);
     const __attribute__((address_space(3))) char* lb =
         (const __attribute__((address_space(3))) char*)smem + stage * STAGE_B;
 
-    f32x16 sacc[KB], pacc[KB];
+    // S^T = K Q^T and dP^T = V dO^T; lane = query row, registers = keys 8(r/4) + 4*h32 + r%4
+    f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      sacc[kb] = f32x16{};
-      pacc[kb] = f32x16{};
-    }
-#pragma unroll
-    for (int k = 0; k < KS; ++k)
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        bf16x8 ka, va;
-        u32x4 u1 = *(const __attribute__((address_space(3))) u32x4*)(lb + (k >> 1) * GB + raddr[k & 1] + kb * 32 * 64);
-        u32x4 u2 = *(const __attribute__((address_space(3))) u32x4*)(lb + TILE_B + (k >> 1) * GB + raddr[k & 1] + kb * 32 * 64);
-        __builtin_memcpy(&ka, &u1, 16);
-        __builtin_memcpy(&va, &u2, 16);
-        sacc[kb] = mfma32(ka, qop[k], sacc[kb]);
-        pacc[kb] = mfma32(va, gop[k], pacc[kb]);
+    for (int k = 0; k < KS; ++k) {
+      bf16x8 ka, va, qv;
+      u32x4 u1 = *(const __attribute__((address_space(3))) u32x4*)(lb + (k >> 1) * GB + raddr[k & 1]);
+      u32x4 u2 = *(const __attribute__((address_space(3))) u32x4*)(lb + TILE_B + (k >> 1) * GB + raddr[k & 1]);
+      __builtin_memcpy(&ka, &u1, 16);
+      __builtin_memcpy(&va, &u2, 16);
+      if (k < QREG) {
+        qv = qop[k];
+      } else {
+        u32x4 uq = *(const __attribute__((address_space(3))) u32x4*)(
+            (const __attribute__((address_space(3))) char*)qlds + (k - QREG) * 1024);
+        __builtin_memcpy(&qv, &uq, 16);
       }
+      sacc = mfma32(ka, qv, sacc);
+      pacc = mfma32(va, gop[k], pacc);
+    }
 
     if (masked) {
-      const int n0 = n * BN_F;
       uint64_t mk = 0;
       for (int si = 0; si < nS; ++si) {
         const Slice sl = load_slice(mv.slices, sidx[si]);
         int lo, hi;
         row_interval(sl, qrow, lo, hi);
-        lo = max(lo, n0);
-        hi = min(hi, n0 + BN_F - 1);
-        if (lo <= hi) mk |= bit_range(lo - n0, hi - n0);
+        lo = max(lo, key0);
+        hi = min(hi, key0 + SK - 1);
+        if (lo <= hi) mk |= bit_range(lo - key0, hi - key0);
       }
-      mk >>= 4 * h32;
+      const uint32_t w = static_cast<uint32_t>(mk >> (4 * h32));
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const uint32_t w = static_cast<uint32_t>(mk >> (32 * kb));
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (!((w >> (8 * (r >> 2) + (r & 3))) & 1u)) sacc[kb][r] = -INFINITY;
-      }
+      for (int r = 0; r < 16; ++r)
+        if (!((w >> (8 * (r >> 2) + (r & 3))) & 1u)) sacc[r] = -INFINITY;
     }
 
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], c, -l2));
-        pacc[kb][r] = pv * (pacc[kb][r] - dval);
-      }
+    for (int r = 0; r < 16; ++r) {
+      const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -l2));
+      pacc[r] = pv * (pacc[r] + ndval);
+    }
 
+    // dQ^T += K^T dS^T over the stage's two 16-key chunks
 #pragma unroll
-    for (int cc = 0; cc < BN_F / 16; ++cc) {
-      const int kb = cc >> 1, c2 = cc & 1;
+    for (int c2 = 0; c2 < 2; ++c2) {
       bf16x8 sb;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sb[e] = static_cast<__bf16>(pacc[kb][8 * c2 + e]);
-      const int roff = (32 * kb + 16 * c2) * 64;
+      for (int e = 0; e < 8; ++e) sb[e] = static_cast<__bf16>(pacc[8 * c2 + e]);
+      const int roff = 16 * c2 * 64;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         const i16x4 k0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lb + mb * GB + taddr[0] + roff));
@@ -440,12 +472,12 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     __syncthreads();
   };
 
-  if (nT > 0) issue(0, 0);
+  if (nU > 0) issue(0, 0);
   wait_dma();
   __syncthreads();
-  for (int t = 0; t < nT; t += 2) {
-    tile(std::integral_constant<int, 0>{}, t);
-    if (t + 1 < nT) tile(std::integral_constant<int, 1>{}, t + 1);
+  for (int u = 0; u < nU; u += 2) {
+    stage_fn(std::integral_constant<int, 0>{}, u);
+    if (u + 1 < nU) stage_fn(std::integral_constant<int, 1>{}, u + 1);
   }
 
   if (qok) {
@@ -491,13 +523,10 @@ hipError_t launch_bwd(const BwdArgs& a, int head_dim, int nq_f, int nk_b, int ph
   }
   const int64_t gq = (int64_t)nq_f * a.Hq;
   if ((phases & FFA_BWD_DQ) && gq > 0) {
-    if (head_dim == 128) {
-      const size_t lds = 2 * 2 * BN_F * 128 * 2;
-      ffa_bwd_dq_kernel<128><<<dim3((unsigned)gq), NT, lds, stream>>>(a);
-    } else {
-      const size_t lds = 2 * 2 * BN_F * 64 * 2;
-      ffa_bwd_dq_kernel<64><<<dim3((unsigned)gq), NT, lds, stream>>>(a);
-    }
+    if (head_dim == 128)
+      ffa_bwd_dq_kernel<128><<<dim3((unsigned)gq), NT, dq_lds_bytes<128>(), stream>>>(a);
+    else
+      ffa_bwd_dq_kernel<64><<<dim3((unsigned)gq), NT, dq_lds_bytes<64>(), stream>>>(a);
   }
   return hipGetLastError();
 }

@@ -352,7 +352,7 @@ struct BwdArgs {
   const __bf16* o;
   const __bf16* dout;
   const float* lse;
-  float* dvec;        // workspace: D_i = dO_i . O_i, [Hq][Tq]
+  float* dvec;        // workspace: -D_i = -dO_i . O_i, [Hq][Tq]
   float* lvec;        // workspace: LSE_i * log2(e) (0 where LSE = -inf), [Hq][Tq]
   __bf16* dq;
   __bf16* dk;

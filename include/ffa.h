@@ -167,7 +167,7 @@ FFA_API ffa_status ffa_fwd(const ffa_shape* shape, ffa_tensor_in q, ffa_tensor_i
                            void* stream);
 
 /* Scratch bytes ffa_bwd needs: per (query head, row) the dot product
- * D_i = dO_i . O_i and LSE_i * log2(e), both fp32. */
+ * -D_i = -(dO_i . O_i) and LSE_i * log2(e), both fp32. */
 FFA_API ffa_status ffa_bwd_workspace_size(const ffa_shape* shape, size_t* bytes);
 
 /* Backward: dq, dk, dv of the forward above, given its o and lse.
@@ -182,7 +182,7 @@ FFA_API ffa_status ffa_bwd(const ffa_shape* shape, ffa_tensor_in q, ffa_tensor_i
                            void* stream);
 
 /* Phases of the backward, for ffa_bwd_phases. */
-#define FFA_BWD_PRE 1   /* D_i = dO_i . O_i and LSE_i log2(e) into d_ws          */
+#define FFA_BWD_PRE 1   /* -D_i = -dO_i . O_i and LSE_i log2(e) into d_ws        */
 #define FFA_BWD_DKDV 2  /* dk, dv (reads D from d_ws)                             */
 #define FFA_BWD_DQ 4    /* dq (reads D from d_ws)                                 */
 #define FFA_BWD_ALL 7
