@@ -79,22 +79,22 @@ class Case:
 def phase_times(cases, reps):
     """Average device time (ms) of each phase, from HIP events on the stream the
     library launches on (torch's current stream)."""
-    names = ["meta", "fwd", "bwd_pre", "bwd_dkdv", "bwd_dq"]
+    # the backward runs as in a step: the dQ kernel with the row statistics
+    # folded in (PRE | DQ), then dK/dV
+    names = ["meta", "fwd", "bwd_dq", "bwd_dkdv"]
     tot = {n: 0.0 for n in names}
     for _ in range(reps):
         for cs in cases:
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
             ev[0].record()
             cs.build_meta()
             ev[1].record()
             cs.fwd()
             ev[2].record()
-            cs.bwd(ffa.BWD_PRE)
+            cs.bwd(ffa.BWD_PRE | ffa.BWD_DQ)
             ev[3].record()
             cs.bwd(ffa.BWD_DKDV)
             ev[4].record()
-            cs.bwd(ffa.BWD_DQ)
-            ev[5].record()
             torch.cuda.synchronize()
             for i, n in enumerate(names):
                 tot[n] += ev[i].elapsed_time(ev[i + 1])
@@ -157,7 +157,7 @@ def profile_phase(cases, phase, reps):
                 elif phase == "bwd_dkdv":
                     cs.bwd(ffa.BWD_DKDV)
                 elif phase == "bwd_dq":
-                    cs.bwd(ffa.BWD_DQ)
+                    cs.bwd(ffa.BWD_PRE | ffa.BWD_DQ)
                 else:
                     raise SystemExit(f"unknown phase {phase}")
     torch.cuda.synchronize()
@@ -229,17 +229,15 @@ def main():
 
     ph = phase_times(cases, max(5, args.steps // 2))
     t_fwd = ph["fwd"] * 1e-3
-    t_bwd = (ph["bwd_pre"] + ph["bwd_dkdv"] + ph["bwd_dq"]) * 1e-3
+    t_bwd = (ph["bwd_dkdv"] + ph["bwd_dq"]) * 1e-3
     # algorithmic FLOPs per kernel: fwd 4d per valid pair and head; of the
-    # backward's 10d, dK/dV take 8d (Q K^T, dO V^T, P^T dO, dS^T Q), dQ 2d (dS K)
+    # backward's 10d, dK/dV take 8d (Q K^T, dO V^T, P^T dO, dS^T Q), dQ 2d (dS K);
+    # the dQ kernel also computes the row statistics -D and LSE log2 e
     alg = {"fwd": f_fwd, "bwd_dkdv": 0.8 * f_bwd, "bwd_dq": 0.2 * f_bwd}
     kernels = {}
     for n in ("fwd", "bwd_dkdv", "bwd_dq"):
         tf = alg[n] / (ph[n] * 1e-3) / 1e12
         kernels[n] = {"ms": round(ph[n], 4), "tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
-    pre_bytes = sum(cs.c.Tq * cs.c.Hq * (2 * 2 * cs.c.d + 4) for cs in cases)
-    kernels["bwd_pre"] = {"ms": round(ph["bwd_pre"], 4),
-                          "gbs": round(pre_bytes / (ph["bwd_pre"] * 1e-3) / 1e9, 1)}
     kernels["meta"] = {"ms": round(ph["meta"], 4)}
     dom = max(("fwd", "bwd_dkdv", "bwd_dq"), key=lambda n: ph[n])
     achieved = kernels[dom]["tflops"]

@@ -312,7 +312,10 @@ constexpr size_t dq_lds_bytes() {
   return 2 * 2 * DQ_SK * D * 2 + (size_t)(NT / 64) * dq_nql<D>() * 1024;
 }
 
-template <int D>
+// PRE: also compute this block's -D and LSE log2 e rows (the bwd_pre work)
+// from the dO operand already in registers and O, use them, and store them
+// for the dK/dV kernel, which then runs after this one.
+template <int D, bool PRE>
 __global__ __launch_bounds__(NT, 3) __attribute__((amdgpu_waves_per_eu(3, 3))) void ffa_bwd_dq_kernel(BwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int SK = DQ_SK;
@@ -361,9 +364,37 @@ __global__ __launch_bounds__(NT, 3) __attribute__((amdgpu_waves_per_eu(3, 3))) v
     }
   }
   float l2 = 0.f, ndval = 0.f;                   // LSE log2(e) and -D of this row
-  if (qok) {
-    l2 = a.lvec[(int64_t)head * a.Tq + qrow];
-    ndval = a.dvec[(int64_t)head * a.Tq + qrow];
+  if constexpr (PRE) {
+    // lanes l32 and l32 + 32 hold the two halves of the row's d
+    float part = 0.f;
+    if (qok) {
+      const __bf16* op = a.o + (int64_t)qrow * a.o_ts + (int64_t)head * a.o_hs + 8 * h32;
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        const u32x4 ou = *reinterpret_cast<const u32x4*>(op + 16 * k);
+        u32x4 gu;
+        __builtin_memcpy(&gu, &gop[k], 16);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          part += __uint_as_float(ou[e] << 16) * __uint_as_float(gu[e] << 16);
+          part += __uint_as_float(ou[e] & 0xffff0000u) * __uint_as_float(gu[e] & 0xffff0000u);
+        }
+      }
+    }
+    ndval = -wave_swap_sum(part);
+    if (qok) {
+      const float l = a.lse[(int64_t)head * a.Tq + qrow];
+      l2 = (l == -INFINITY) ? 0.f : l * LOG2E;
+      if (h32 == 0) {
+        a.dvec[(int64_t)head * a.Tq + qrow] = ndval;
+        a.lvec[(int64_t)head * a.Tq + qrow] = l2;
+      }
+    }
+  } else {
+    if (qok) {
+      l2 = a.lvec[(int64_t)head * a.Tq + qrow];
+      ndval = a.dvec[(int64_t)head * a.Tq + qrow];
+    }
   }
   wait_vmem();
   char* qlds = smem + 2 * STAGE_B + wid * (NQL * 1024) + lane * 16;
@@ -505,13 +536,22 @@ __global__ __launch_bounds__(NT, 3) __attribute__((amdgpu_waves_per_eu(3, 3))) v
 hipError_t launch_bwd(const BwdArgs& a, int head_dim, int nq_f, int nk_b, int phases,
                       hipStream_t stream) {
   const int64_t rows = (int64_t)a.Tq * a.Hq;
-  if ((phases & FFA_BWD_PRE) && rows > 0) {
+  const int64_t gk = (int64_t)nk_b * a.Hkv;
+  const int64_t gq = (int64_t)nq_f * a.Hq;
+  // PRE together with DQ: the dQ kernel computes the row statistics itself and
+  // runs first; otherwise PRE is its own kernel.
+  const bool fused = (phases & FFA_BWD_PRE) && (phases & FFA_BWD_DQ) && gq > 0;
+  if (fused) {
+    if (head_dim == 128)
+      ffa_bwd_dq_kernel<128, true><<<dim3((unsigned)gq), NT, dq_lds_bytes<128>(), stream>>>(a);
+    else
+      ffa_bwd_dq_kernel<64, true><<<dim3((unsigned)gq), NT, dq_lds_bytes<64>(), stream>>>(a);
+  } else if ((phases & FFA_BWD_PRE) && rows > 0) {
     const int G = head_dim / 8;
     const int64_t blocks = (rows * G + NT - 1) / NT;
     if (head_dim == 128) ffa_bwd_pre_kernel<128><<<dim3((unsigned)blocks), NT, 0, stream>>>(a);
     else ffa_bwd_pre_kernel<64><<<dim3((unsigned)blocks), NT, 0, stream>>>(a);
   }
-  const int64_t gk = (int64_t)nk_b * a.Hkv;
   if ((phases & FFA_BWD_DKDV) && gk > 0) {
     if (head_dim == 128) {
       const size_t lds = 2 * (2 * BM_B * 128 * 2 + 2 * BM_B * 4);
@@ -521,12 +561,11 @@ hipError_t launch_bwd(const BwdArgs& a, int head_dim, int nq_f, int nk_b, int ph
       ffa_bwd_dkdv_kernel<64><<<dim3((unsigned)gk), NT, lds, stream>>>(a);
     }
   }
-  const int64_t gq = (int64_t)nq_f * a.Hq;
-  if ((phases & FFA_BWD_DQ) && gq > 0) {
+  if (!fused && (phases & FFA_BWD_DQ) && gq > 0) {
     if (head_dim == 128)
-      ffa_bwd_dq_kernel<128><<<dim3((unsigned)gq), NT, dq_lds_bytes<128>(), stream>>>(a);
+      ffa_bwd_dq_kernel<128, false><<<dim3((unsigned)gq), NT, dq_lds_bytes<128>(), stream>>>(a);
     else
-      ffa_bwd_dq_kernel<64><<<dim3((unsigned)gq), NT, dq_lds_bytes<64>(), stream>>>(a);
+      ffa_bwd_dq_kernel<64, false><<<dim3((unsigned)gq), NT, dq_lds_bytes<64>(), stream>>>(a);
   }
   return hipGetLastError();
 }

@@ -187,10 +187,12 @@ FFA_API ffa_status ffa_bwd(const ffa_shape* shape, ffa_tensor_in q, ffa_tensor_i
 #define FFA_BWD_DQ 4    /* dq (reads D from d_ws)                                 */
 #define FFA_BWD_ALL 7
 
-/* ffa_bwd restricted to a subset of its phases (bitwise OR of FFA_BWD_*), in
- * the order PRE, DKDV, DQ.  DKDV and DQ read the D values that PRE wrote into
- * the same d_ws; DKDV and DQ are independent of each other, so a caller may
- * run them on two streams once PRE has finished.  phases = FFA_BWD_ALL is
+/* ffa_bwd restricted to a subset of its phases (bitwise OR of FFA_BWD_*).
+ * DKDV and DQ read the values that PRE wrote into the same d_ws; once PRE has
+ * finished they are independent of each other, so a caller may run them on
+ * two streams.  When PRE and DQ are requested together, the dQ kernel
+ * computes the PRE values itself, stores them in d_ws, and runs first, then
+ * DKDV; otherwise the order is PRE, DKDV, DQ.  phases = FFA_BWD_ALL is
  * ffa_bwd.  Unknown bits give FFA_ERR_INVALID_ARGUMENT. */
 FFA_API ffa_status ffa_bwd_phases(const ffa_shape* shape, ffa_tensor_in q, ffa_tensor_in k,
                                   ffa_tensor_in v, ffa_tensor_in o, const float* lse,

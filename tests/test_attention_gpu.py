@@ -114,6 +114,30 @@ def test_random_tables(d, seed):
     full_check(c, wl.make_tensors(c, 1000 + seed))
 
 
+def test_backward_phases_separately_match_one_call():
+    """PRE, DKDV and DQ run as three calls (standalone row-statistics kernel)
+    give the gradients of the single call (row statistics folded into dQ),
+    up to the summation order of D."""
+    rng = random.Random(77)
+    Tq, Tk = 700, 650
+    sl = wl.random_slices(rng, Tq, Tk, 5)
+    c = wl.Call(sl, Tq, Tk, 4, 2, 128)
+    T = wl.make_tensors(c, 77)
+    q, k, v, do = (T[n].to(DEV) for n in ("q", "k", "v", "do"))
+    meta = ffa.build_meta(sl, Tq, Tk, 128)
+    o, lse = ffa.fwd(q, k, v, meta)
+    g1 = ffa.bwd(q, k, v, o, lse, do, meta)
+    ws = torch.empty(ffa.bwd_workspace_size(q, k), dtype=torch.uint8, device=DEV)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    for ph in (ffa.BWD_PRE, ffa.BWD_DKDV, ffa.BWD_DQ):
+        ffa.bwd(q, k, v, o, lse, do, meta, dq=dq, dk=dk, dv=dv, workspace=ws, phases=ph)
+    torch.cuda.synchronize()
+    for a, b, n in zip(g1, (dq, dk, dv), ("dQ", "dK", "dV")):
+        a64, b64 = a.double(), b.double()
+        rel = float((a64 - b64).norm() / max(float(a64.norm()), 1e-30))
+        assert rel <= 1e-3, f"{n}: phased vs single call relative difference {rel:.3g}"
+
+
 def test_every_mask_type_lq_ne_lk():
     sl = [(0, 100, 0, 300, wl.CAUSAL), (100, 300, 300, 400, wl.CAUSAL),        # Lq > Lk: empty first rows
           (300, 450, 0, 200, wl.INV_CAUSAL), (450, 700, 400, 500, wl.INV_CAUSAL),
