@@ -1,21 +1,27 @@
 """Build libffa.so (HIP for gfx950) in-tree with hipcc.
 
 Usage: python -m flexible_mask_attention_amd._build   (or __graft_entry__.build()).
+
+Each source is compiled to an object of its own (in parallel, with the flags
+below plus any per-file extras), then the objects are linked into the shared
+library next to this file.
 """
 from __future__ import annotations
 
 import os
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libffa.so")
-SOURCES = ["ffa_api.hip", "ffa_meta.hip", "ffa_fwd.hip", "ffa_bwd.hip"]
+SOURCES = ["ffa_api.hip", "ffa_meta.hip", "ffa_fwd.hip", "ffa_bwd.hip", "ffa_bwd_dkdv.hip"]
 ARCH = os.environ.get("FFA_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-fvisibility=hidden", "-Wall", "-Wno-unused-function",
     # keep the compiler from forming packed fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -23,6 +29,15 @@ FLAGS = [
     # accumulation registers and the VGPRs that the softmax arithmetic reads
     "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
+
+# Per-file extras.  The dK/dV kernel measured faster with the scheduler's
+# memory-clause strategy (the forward and dQ kernels slower), so only its file
+# gets it.
+EXTRA = {
+    "ffa_bwd_dkdv.hip": ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"],
+}
+
+NOISE = "is not a recognized feature for this target"
 
 
 def hipcc() -> str:
@@ -32,22 +47,29 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    objs = []
-    tmp = LIB + ".tmp"
-    cmd = [hipcc()] + FLAGS + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(ln for ln in (r.stderr or "").splitlines() if noise not in ln)
+    err = "\n".join(ln for ln in (r.stderr or "").splitlines() if NOISE not in ln)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
     if err.strip() and verbose:
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    del objs
-    return LIB
+
+
+def build(verbose: bool = False, csrc: str = CSRC, out: str = LIB) -> str:
+    with tempfile.TemporaryDirectory(prefix="ffa_build_") as tmp:
+        objs = [os.path.join(tmp, s + ".o") for s in SOURCES]
+        cmds = [[hipcc()] + FLAGS + EXTRA.get(s, []) + ["-c", os.path.join(csrc, s), "-o", o]
+                for s, o in zip(SOURCES, objs)]
+        with ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 1)) as ex:
+            for f in [ex.submit(_run, c, verbose) for c in cmds]:
+                f.result()
+        tmp_lib = out + ".tmp"
+        _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC"] + objs + ["-o", tmp_lib], verbose)
+        os.replace(tmp_lib, out)
+    return out
 
 
 if __name__ == "__main__":

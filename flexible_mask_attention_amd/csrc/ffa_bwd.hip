@@ -8,17 +8,12 @@
 // reproducible results without atomics:
 //
 //   bwd_pre : -D_i = -dO_i . O_i, LSE_i log2 e          (fp32, [Hq][Tq])
-//   dkdv    : owner (kv head, 128-key block); loops over the query heads that
-//             share the kv head and the k2q tiles of the block, in list order:
-//             S = Q K^T, P = exp(S - LSE) (masked on Partial tiles),
-//             dV += P^T dO, dP = dO V^T, dS = P (dP - D), dK += dS^T Q
+//   dkdv    : owner (kv head, 128-key block), in ffa_bwd_dkdv.hip
 //   dq      : owner (query head, 128-row block); loops over its q2k tiles:
 //             S^T, P^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T
 //
-// MFMA orientation: in dkdv each lane owns one key (S = Q K^T leaves keys on
-// lanes), so P and dS feed the dV^T / dK^T MFMAs as B operands and dO^T, Q^T
-// come from LDS through transposed reads.  dq mirrors the forward (lanes own
-// query rows).
+// dq mirrors the forward (lanes own query rows).  This file also holds the
+// backward's launcher.
 #include <type_traits>
 
 #include "ffa_internal.hpp"
@@ -57,238 +52,6 @@ __global__ __launch_bounds__(NT) void ffa_bwd_pre_kernel(BwdArgs a) {
     a.dvec[(int64_t)h * a.Tq + i] = -acc;
     const float l = a.lse[(int64_t)h * a.Tq + i];
     a.lvec[(int64_t)h * a.Tq + i] = (l == -INFINITY) ? 0.f : l * LOG2E;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// dK, dV: owner (kv head, BN_B-key block), 4 waves x 32 keys.
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void ffa_bwd_dkdv_kernel(BwdArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  constexpr int TILE_B = BM_B * D * 2;          // bytes of one Q or dO tile
-  constexpr int STAGE_B = 2 * TILE_B + 2 * BM_B * 4;
-  constexpr int QB = BM_B / 32;                 // 32-row query blocks per tile
-  constexpr int MB = D / 32;
-  constexpr int KS = D / 16;
-
-  const MetaView mv = meta_view(a.meta);
-  const FFA_CONST MetaHeader* hd = mv.hdr;
-  if (hd->status != 0 || hd->seqlen_q != a.Tq || hd->seqlen_k != a.Tk) return;
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, h32 = lane >> 5, t16 = lane & 15, g16 = lane >> 4;
-  int item, kvh;
-  xcd_map(blockIdx.x, a.Hkv, item, kvh);
-  const int n = mv.sched_b[item];
-  const int key = n * BN_B + wid * 32 + l32;
-  const bool kok = key < a.Tk;
-  const int G = a.Hq / a.Hkv;
-
-  const int f0 = mv.kf_off[n], nF = mv.kf_off[n + 1] - f0;
-  const int p0 = mv.km_off[n], nP = mv.km_off[n + 1] - p0;
-  const int nT = nP + nF;
-  cint32_t* fidx = mv.var + hd->list_off[L_KF] + f0;
-  cint32_t* pidx = mv.var + hd->list_off[L_KM] + p0;
-
-  // K and V as B operands: lane holds K[key][16k + 8*h32 + e]
-  bf16x8 kop[KS], vop[KS];
-  {
-    const __bf16* kp = a.k + (int64_t)key * a.k_ts + (int64_t)kvh * a.k_hs + 8 * h32;
-    const __bf16* vp = a.v + (int64_t)key * a.v_ts + (int64_t)kvh * a.v_hs + 8 * h32;
-#pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      u32x4 u = kok ? *reinterpret_cast<const u32x4*>(kp + 16 * k) : u32x4{0, 0, 0, 0};
-      u32x4 w = kok ? *reinterpret_cast<const u32x4*>(vp + 16 * k) : u32x4{0, 0, 0, 0};
-      __builtin_memcpy(&kop[k], &u, 16);
-      __builtin_memcpy(&vop[k], &w, 16);
-    }
-  }
-
-  wait_vmem();
-
-  // loop-invariant LDS read bases: the 128-bit read of chunk 2k + h32 of row
-  // l32 is at (k / 2) * GB + raddr[k % 2], the transposed read of rows 8j..
-  // of column group mb at mb * GB + taddr[j] (row offsets are immediates)
-  constexpr int GB = group_bytes<BM_B>();
-  int raddr[2], taddr[2];
-#pragma unroll
-  for (int p = 0; p < 2; ++p) raddr[p] = lds_pos(l32, 2 * p + h32);
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-    taddr[j] = lds_pos(4 * h32 + (t16 >> 2) + 8 * j, 2 * (g16 & 1) + ((t16 >> 1) & 1)) + 8 * (t16 & 1);
-  const int laddr = 2 * TILE_B + 16 * h32;   // row-stat reads: + (32qb + 8j) * 4
-
-  TileDma<D, BM_B> dq_dma, dg_dma;
-  dq_dma.init(wid, lane, a.q_ts);
-  dg_dma.init(wid, lane, a.do_ts);
-
-  f32x16 dkacc[MB], dvacc[MB];
-#pragma unroll
-  for (int i = 0; i < MB; ++i) {
-    dkacc[i] = f32x16{};
-    dvacc[i] = f32x16{};
-  }
-
-  // Step u covers query head kvh*G + u % G of list entry nT - 1 - u / G: the
-  // lists (Partial, then Full, ascending) are walked backwards and the heads
-  // sharing this key head are interleaved, so every key block of a causal
-  // sequence starts at the sequence's last query tile and the blocks resident
-  // on one XCD move through the same Q / dO tiles at about the same time.
-  const int total = G * nT;
-  auto tile_of = [&](int t) { return t < nP ? pidx[t] : fidx[t - nP]; };
-  auto issue = [&](int u, int stage) {
-    const int hq = kvh * G + u % G;
-    const int m = tile_of(nT - 1 - u / G);
-    char* st = smem + stage * STAGE_B;
-    const int vr = a.Tq - m * BM_B;
-    dq_dma.load(a.q + (int64_t)hq * a.q_hs, a.q_ts, m * BM_B, vr, st);
-    dg_dma.load(a.dout + (int64_t)hq * a.do_hs, a.do_ts, m * BM_B, vr, st + TILE_B);
-    if (wid < 2) {
-      const float* src = (wid == 0 ? a.lvec : a.dvec) + (int64_t)hq * a.Tq + m * BM_B;
-      const int rows = vr < 0 ? 0 : (vr > BM_B ? BM_B : vr);
-      const i32x4 r = make_rsrc(src, (uint32_t)(rows * 4));
-      dma4(r, st + 2 * TILE_B + wid * BM_B * 4, lane * 4);
-    }
-  };
-  const float c = a.scale_log2;
-
-  auto tile = [&](auto stage_c, int u) {
-    constexpr int stage = decltype(stage_c)::value;
-    const int t = nT - 1 - u / G;
-    const bool masked = t < nP;
-    const int m = tile_of(t);
-    if (u + 1 < total) issue(u + 1, stage ^ 1);
-    const __attribute__((address_space(3))) char* lb =
-        (const __attribute__((address_space(3))) char*)smem + stage * STAGE_B;
-
-    // Partial tile: valid rows of this key inside [m0, m0 + BM_B) from the
-    // slices of the enclosing forward query block, one bit per row
-    uint64_t mk = 0;
-    if (masked) {
-      const int m0 = m * BM_B;
-      const int mf = m0 / BM_F;
-      const int s0 = mv.qs_off[mf], nS = mv.qs_off[mf + 1] - s0;
-      cint32_t* sidx = mv.var + hd->list_off[L_QS] + s0;
-      for (int si = 0; si < nS; ++si) {
-        const Slice sl = load_slice(mv.slices, sidx[si]);
-        int lo, hi;
-        col_interval(sl, key, lo, hi);
-        lo = max(lo, m0);
-        hi = min(hi, m0 + BM_B - 1);
-        if (lo <= hi) mk |= bit_range(lo - m0, hi - m0);
-      }
-      mk >>= 4 * h32;
-    }
-
-    // one 32-row half at a time, so that only one S / dP pair is live
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      // S = Q K^T and dP - D = dO V^T - D; lane = key, registers = rows
-      // 32qb + 8(r/4) + 4*h32 + r%4.  The dP accumulator starts at -D (four
-      // 128-bit LDS reads), which saves the subtraction in dS = P (dP - D).
-      f32x16 sacc = f32x16{}, pacc;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 nd = *(const __attribute__((address_space(3))) f32x4*)(
-            lb + laddr + (32 * qb + 8 * j) * 4 + BM_B * 4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pacc[4 * j + i] = nd[i];
-      }
-#pragma unroll
-      for (int k = 0; k < KS; ++k) {
-        bf16x8 qa, ga;
-        u32x4 u1 = *(const __attribute__((address_space(3))) u32x4*)(lb + (k >> 1) * GB + raddr[k & 1] + qb * 32 * 64);
-        u32x4 u2 = *(const __attribute__((address_space(3))) u32x4*)(lb + TILE_B + (k >> 1) * GB + raddr[k & 1] + qb * 32 * 64);
-        __builtin_memcpy(&qa, &u1, 16);
-        __builtin_memcpy(&ga, &u2, 16);
-        sacc = mfma32(qa, kop[k], sacc);
-        pacc = mfma32(ga, vop[k], pacc);
-      }
-      if (masked) {
-        const uint32_t w = static_cast<uint32_t>(mk >> (32 * qb));
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (!((w >> (8 * (r >> 2) + (r & 3))) & 1u)) sacc[r] = -INFINITY;
-      }
-
-      // P = exp2(S c - LSE log2 e), dS = P (dP - D)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 l4 = *(const __attribute__((address_space(3))) f32x4*)(lb + laddr + (32 * qb + 8 * j) * 4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * j + i;
-          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -l4[i]));
-          sacc[r] = pv;
-          pacc[r] *= pv;
-        }
-      }
-
-      // dV^T += dO^T P and dK^T += Q^T dS over the half's two 16-row chunks
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        bf16x8 pb, sb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pb[e] = static_cast<__bf16>(sacc[8 * c2 + e]);
-          sb[e] = static_cast<__bf16>(pacc[8 * c2 + e]);
-        }
-        const int roff = (32 * qb + 16 * c2) * 64;
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const i16x4 g0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lb + TILE_B + mb * GB + taddr[0] + roff));
-          const i16x4 g1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lb + TILE_B + mb * GB + taddr[1] + roff));
-          const i16x4 q0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lb + mb * GB + taddr[0] + roff));
-          const i16x4 q1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lb + mb * GB + taddr[1] + roff));
-          const i16x8 gg = __builtin_shufflevector(g0, g1, 0, 1, 2, 3, 4, 5, 6, 7);
-          const i16x8 qq = __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7);
-          bf16x8 ga, qa;
-          __builtin_memcpy(&ga, &gg, 16);
-          __builtin_memcpy(&qa, &qq, 16);
-          dvacc[mb] = mfma32(ga, pb, dvacc[mb]);
-          dkacc[mb] = mfma32(qa, sb, dkacc[mb]);
-        }
-      }
-    }
-    wait_dma();
-    __syncthreads();
-  };
-
-  if (total > 0) issue(0, 0);
-  wait_dma();
-  __syncthreads();
-  for (int u = 0; u < total; u += 2) {
-    tile(std::integral_constant<int, 0>{}, u);
-    if (u + 1 < total) tile(std::integral_constant<int, 1>{}, u + 1);
-  }
-
-  if (kok) {
-    // FFA_ACCUMULATE: add to what dk / dv hold (fp32 sum, one rounding)
-    const bool acc = (a.flags & FFA_ACCUMULATE) != 0;
-    __bf16* kp = a.dk + (int64_t)key * a.dk_ts + (int64_t)kvh * a.dk_hs;
-    __bf16* vp = a.dv + (int64_t)key * a.dv_ts + (int64_t)kvh * a.dv_hs;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        bf16x4* dk4 = reinterpret_cast<bf16x4*>(kp + 32 * mb + 8 * j + 4 * h32);
-        bf16x4* dv4 = reinterpret_cast<bf16x4*>(vp + 32 * mb + 8 * j + 4 * h32);
-        bf16x4 ok = bf16x4{}, ov = bf16x4{};
-        if (acc) {
-          ok = *dk4;
-          ov = *dv4;
-        }
-        bf16x4 wk, wv;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          wk[i] = static_cast<__bf16>(dkacc[mb][4 * j + i] * a.scale + static_cast<float>(ok[i]));
-          wv[i] = static_cast<__bf16>(dvacc[mb][4 * j + i] + static_cast<float>(ov[i]));
-        }
-        *dk4 = wk;
-        *dv4 = wv;
-      }
   }
 }
 
@@ -553,13 +316,8 @@ hipError_t launch_bwd(const BwdArgs& a, int head_dim, int nq_f, int nk_b, int ph
     else ffa_bwd_pre_kernel<64><<<dim3((unsigned)blocks), NT, 0, stream>>>(a);
   }
   if ((phases & FFA_BWD_DKDV) && gk > 0) {
-    if (head_dim == 128) {
-      const size_t lds = 2 * (2 * BM_B * 128 * 2 + 2 * BM_B * 4);
-      ffa_bwd_dkdv_kernel<128><<<dim3((unsigned)gk), NT, lds, stream>>>(a);
-    } else {
-      const size_t lds = 2 * (2 * BM_B * 64 * 2 + 2 * BM_B * 4);
-      ffa_bwd_dkdv_kernel<64><<<dim3((unsigned)gk), NT, lds, stream>>>(a);
-    }
+    const hipError_t e = launch_bwd_dkdv(a, head_dim, gk, stream);
+    if (e != hipSuccess) return e;
   }
   if (!fused && (phases & FFA_BWD_DQ) && gq > 0) {
     if (head_dim == 128)

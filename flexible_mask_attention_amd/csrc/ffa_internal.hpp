@@ -367,5 +367,6 @@ struct BwdArgs {
 };
 hipError_t launch_bwd(const BwdArgs& a, int head_dim, int nq_f, int nk_b, int phases,
                       hipStream_t stream);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int64_t grid, hipStream_t stream);
 
 }  // namespace ffa
