@@ -11,7 +11,7 @@
 // dV^T / dK^T MFMAs as B operands and dO^T, Q^T come from LDS through
 // transposed reads.  This file is compiled on its own so that it can use the
 // memory-clause scheduling strategy, which measured faster for this kernel
-// (and slower for the others).
+// (the dQ kernel spills with it).
 #include <type_traits>
 
 #include "ffa_internal.hpp"
