@@ -203,26 +203,11 @@ __global__ __launch_bounds__(NT, 3) __attribute__((amdgpu_waves_per_eu(3, 3))) v
     const __attribute__((address_space(3))) char* lb =
         (const __attribute__((address_space(3))) char*)smem + stage * STAGE_B;
 
-    // S^T = K Q^T and dP^T = V dO^T; lane = query row, registers = keys 8(r/4) + 4*h32 + r%4
-    f32x16 sacc = f32x16{}, pacc = f32x16{};
-#pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      bf16x8 ka, va, qv;
-      u32x4 u1 = *(const __attribute__((address_space(3))) u32x4*)(lb + (k >> 1) * GB + raddr[k & 1]);
-      u32x4 u2 = *(const __attribute__((address_space(3))) u32x4*)(lb + TILE_B + (k >> 1) * GB + raddr[k & 1]);
-      __builtin_memcpy(&ka, &u1, 16);
-      __builtin_memcpy(&va, &u2, 16);
-      if (k < QREG) {
-        qv = qop[k];
-      } else {
-        u32x4 uq = *(const __attribute__((address_space(3))) u32x4*)(
-            (const __attribute__((address_space(3))) char*)qlds + (k - QREG) * 1024);
-        __builtin_memcpy(&qv, &uq, 16);
-      }
-      sacc = mfma32(ka, qv, sacc);
-      pacc = mfma32(va, gop[k], pacc);
-    }
-
+    // Partial tile: valid keys of this lane's row inside [key0, key0 + SK), one
+    // bit per key.  A stage with no valid pair for any of the wave's rows is
+    // skipped: it would add nothing.
+    uint32_t w = ~0u;
+    bool live = true;
     if (masked) {
       uint64_t mk = 0;
       for (int si = 0; si < nS; ++si) {
@@ -233,33 +218,58 @@ __global__ __launch_bounds__(NT, 3) __attribute__((amdgpu_waves_per_eu(3, 3))) v
         hi = min(hi, key0 + SK - 1);
         if (lo <= hi) mk |= bit_range(lo - key0, hi - key0);
       }
-      const uint32_t w = static_cast<uint32_t>(mk >> (4 * h32));
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (!((w >> (8 * (r >> 2) + (r & 3))) & 1u)) sacc[r] = -INFINITY;
+      live = __ballot(mk != 0) != 0;
+      w = static_cast<uint32_t>(mk >> (4 * h32));
     }
 
+    if (live) {
+      // S^T = K Q^T and dP^T = V dO^T; lane = query row, registers = keys 8(r/4) + 4*h32 + r%4
+      f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -l2));
-      pacc[r] = pv * (pacc[r] + ndval);
-    }
+      for (int k = 0; k < KS; ++k) {
+        bf16x8 ka, va, qv;
+        u32x4 u1 = *(const __attribute__((address_space(3))) u32x4*)(lb + (k >> 1) * GB + raddr[k & 1]);
+        u32x4 u2 = *(const __attribute__((address_space(3))) u32x4*)(lb + TILE_B + (k >> 1) * GB + raddr[k & 1]);
+        __builtin_memcpy(&ka, &u1, 16);
+        __builtin_memcpy(&va, &u2, 16);
+        if (k < QREG) {
+          qv = qop[k];
+        } else {
+          u32x4 uq = *(const __attribute__((address_space(3))) u32x4*)(
+              (const __attribute__((address_space(3))) char*)qlds + (k - QREG) * 1024);
+          __builtin_memcpy(&qv, &uq, 16);
+        }
+        sacc = mfma32(ka, qv, sacc);
+        pacc = mfma32(va, gop[k], pacc);
+      }
+      if (masked) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (!((w >> (8 * (r >> 2) + (r & 3))) & 1u)) sacc[r] = -INFINITY;
+      }
 
-    // dQ^T += K^T dS^T over the stage's two 16-key chunks
 #pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2) {
-      bf16x8 sb;
+      for (int r = 0; r < 16; ++r) {
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -l2));
+        pacc[r] = pv * (pacc[r] + ndval);
+      }
+
+      // dQ^T += K^T dS^T over the stage's two 16-key chunks
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sb[e] = static_cast<__bf16>(pacc[8 * c2 + e]);
-      const int roff = 16 * c2 * 64;
+      for (int c2 = 0; c2 < 2; ++c2) {
+        bf16x8 sb;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const i16x4 k0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lb + mb * GB + taddr[0] + roff));
-        const i16x4 k1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lb + mb * GB + taddr[1] + roff));
-        const i16x8 kk = __builtin_shufflevector(k0, k1, 0, 1, 2, 3, 4, 5, 6, 7);
-        bf16x8 ka;
-        __builtin_memcpy(&ka, &kk, 16);
-        dqacc[mb] = mfma32(ka, sb, dqacc[mb]);
+        for (int e = 0; e < 8; ++e) sb[e] = static_cast<__bf16>(pacc[8 * c2 + e]);
+        const int roff = 16 * c2 * 64;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const i16x4 k0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lb + mb * GB + taddr[0] + roff));
+          const i16x4 k1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lb + mb * GB + taddr[1] + roff));
+          const i16x8 kk = __builtin_shufflevector(k0, k1, 0, 1, 2, 3, 4, 5, 6, 7);
+          bf16x8 ka;
+          __builtin_memcpy(&ka, &kk, 16);
+          dqacc[mb] = mfma32(ka, sb, dqacc[mb]);
+        }
       }
     }
     wait_dma();

@@ -126,8 +126,9 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         (const __attribute__((address_space(3))) char*)smem + stage * STAGE_B;
 
     // Partial tile: valid rows of this key inside [m0, m0 + BM_B) from the
-    // slices of the enclosing forward query block, one bit per row
-    uint64_t mk = 0;
+    // slices of the enclosing forward query block, one bit per row.  A half
+    // with no valid pair for any of the wave's keys is skipped.
+    uint64_t mk = 0, mkf = 0;
     if (masked) {
       const int m0 = m * BM_B;
       const int mf = m0 / BM_F;
@@ -141,12 +142,14 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         hi = min(hi, m0 + BM_B - 1);
         if (lo <= hi) mk |= bit_range(lo - m0, hi - m0);
       }
+      mkf = mk;
       mk >>= 4 * h32;
     }
 
     // one 32-row half at a time, so that only one S / dP pair is live
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
+      if (masked && __ballot(((mkf >> (32 * qb)) & 0xffffffffull) != 0) == 0) continue;
       // S = Q K^T and dP - D = dO V^T - D; lane = key, registers = rows
       // 32qb + 8(r/4) + 4*h32 + r%4.  The dP accumulator starts at -D (four
       // 128-bit LDS reads), which saves the subtraction in dS = P (dP - D).

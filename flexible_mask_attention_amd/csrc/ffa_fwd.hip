@@ -30,9 +30,8 @@ namespace {
 constexpr int NW = 4;                 // waves per block
 constexpr int NT = 64 * NW;
 constexpr int RW = BM_F / NW;         // query rows per wave
-constexpr int QB = RW / 32;           // 32-row MFMA blocks per wave
 constexpr int SK = 32;                // keys per stage
-static_assert(QB == 1 && BN_F % SK == 0 && 2 * SK == 16 * NW, "forward tiling");
+static_assert(RW == 32 && BN_F % SK == 0 && 2 * SK == 16 * NW, "forward tiling");
 
 template <int D>
 __global__ __launch_bounds__(NT, 3) __attribute__((amdgpu_waves_per_eu(3, 3)))
@@ -56,7 +55,7 @@ void ffa_fwd_kernel(FwdArgs a) {
   xcd_map(blockIdx.x, a.Hq, item, head);
   const int m = mv.sched_f[item];
   const int kvh = head / (a.Hq / a.Hkv);
-  const int row0 = m * BM_F + wid * RW + l32;   // row of block qb: row0 + 32 qb
+  const int row0 = m * BM_F + wid * RW + l32;   // this lane's query row
 
   const int f0 = mv.qf_off[m], nF = mv.qf_off[m + 1] - f0;
   const int p0 = mv.qm_off[m], nP = mv.qm_off[m + 1] - p0;
@@ -66,16 +65,14 @@ void ffa_fwd_kernel(FwdArgs a) {
   const int s0 = mv.qs_off[m], nS = mv.qs_off[m + 1] - s0;
   cint32_t* sidx = mv.var + hd->list_off[L_QS] + s0;
 
-  // Q^T operands: lane holds Q[row0 + 32qb][16k + 8*h32 + e]
-  bf16x8 qop[QB][KS];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qrow = row0 + 32 * qb;
-    const __bf16* qp = a.q + (int64_t)qrow * a.q_ts + (int64_t)head * a.q_hs + 8 * h32;
+  // Q^T operand: lane holds Q[row0][16k + 8*h32 + e]
+  bf16x8 qop[KS];
+  {
+    const __bf16* qp = a.q + (int64_t)row0 * a.q_ts + (int64_t)head * a.q_hs + 8 * h32;
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
-      u32x4 u = qrow < a.Tq ? *reinterpret_cast<const u32x4*>(qp + 16 * k) : u32x4{0, 0, 0, 0};
-      __builtin_memcpy(&qop[qb][k], &u, 16);
+      u32x4 u = row0 < a.Tq ? *reinterpret_cast<const u32x4*>(qp + 16 * k) : u32x4{0, 0, 0, 0};
+      __builtin_memcpy(&qop[k], &u, 16);
     }
   }
 
@@ -104,17 +101,10 @@ void ffa_fwd_kernel(FwdArgs a) {
     else dm.load(vbase, a.v_ts, key0, a.Tk - key0, st + TILE_B);
   };
 
-  f32x16 oacc[QB][MB];
+  f32x16 oacc[MB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int i = 0; i < MB; ++i) oacc[qb][i] = f32x16{};
-  float m_run[QB], l_run[QB];             // running max of raw scores, partial row sum
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = -INFINITY;
-    l_run[qb] = 0.f;
-  }
+  for (int i = 0; i < MB; ++i) oacc[i] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;   // running max of raw scores, partial row sum
   const float c = a.scale_log2;           // > 0
   const float thr = 8.f / c;              // rescale only when the max grows by 2^8
 
@@ -127,82 +117,80 @@ void ffa_fwd_kernel(FwdArgs a) {
     const __attribute__((address_space(3))) char* lb =
         (const __attribute__((address_space(3))) char*)smem + stage * STAGE_B;
 
-    // S^T = K Q^T
-    f32x16 sacc[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) sacc[qb] = f32x16{};
-#pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      u32x4 u4 = *(const __attribute__((address_space(3))) u32x4*)(lb + (k >> 1) * GB + kaddr[k & 1]);
-      bf16x8 kop;
-      __builtin_memcpy(&kop, &u4, 16);
-      sacc[0] = mfma32(kop, qop[0][k], sacc[0]);
+    // Partial tile: valid keys of this wave's row inside [key0, key0 + SK),
+    // one bit per key.  A stage with no valid pair for any of the wave's rows
+    // (e.g. above a causal diagonal) is skipped: it would add nothing.
+    uint32_t w = ~0u;
+    bool live = true;
+    if (masked) {
+      uint64_t mk = 0;
+      for (int si = 0; si < nS; ++si) {
+        const Slice sl = load_slice(mv.slices, sidx[si]);
+        int lo, hi;
+        row_interval(sl, row0, lo, hi);
+        lo = max(lo, key0);
+        hi = min(hi, key0 + SK - 1);
+        if (lo <= hi) mk |= bit_range(lo - key0, hi - key0);
+      }
+      live = __ballot(mk != 0) != 0;
+      w = static_cast<uint32_t>(mk >> (4 * h32));   // register r holds key 8(r/4) + 4*h32 + r%4
     }
 
-    if (masked) {
-      // keys of row row0 + 32qb inside [key0, key0 + SK), one bit per key;
-      // register r holds key 8(r/4) + 4*h32 + r%4
+    if (live) {
+      // S^T = K Q^T
+      f32x16 sacc = f32x16{};
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const int qrow = row0 + 32 * qb;
-        uint64_t mk = 0;
-        for (int si = 0; si < nS; ++si) {
-          const Slice sl = load_slice(mv.slices, sidx[si]);
-          int lo, hi;
-          row_interval(sl, qrow, lo, hi);
-          lo = max(lo, key0);
-          hi = min(hi, key0 + SK - 1);
-          if (lo <= hi) mk |= bit_range(lo - key0, hi - key0);
-        }
-        const uint32_t w = static_cast<uint32_t>(mk >> (4 * h32));
+      for (int k = 0; k < KS; ++k) {
+        u32x4 u4 = *(const __attribute__((address_space(3))) u32x4*)(lb + (k >> 1) * GB + kaddr[k & 1]);
+        bf16x8 kop;
+        __builtin_memcpy(&kop, &u4, 16);
+        sacc = mfma32(kop, qop[k], sacc);
+      }
+      if (masked) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (!((w >> (8 * (r >> 2) + (r & 3))) & 1u)) sacc[qb][r] = -INFINITY;
+          if (!((w >> (8 * (r >> 2) + (r & 3))) & 1u)) sacc[r] = -INFINITY;
       }
-    }
 
-    bf16x8 pop[QB][2];
+      float mx = sacc[0];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = sacc[qb][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[qb][r]);
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
       mx = wave_swap_max(mx);
-      if (__ballot(mx > m_run[qb] + thr) != 0) {
-        const float m_new = fmaxf(m_run[qb], mx);
-        const float alpha = (m_run[qb] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run[qb] - m_new) * c);
-        l_run[qb] *= alpha;
+      if (__ballot(mx > m_run + thr) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
+        l_run *= alpha;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[qb][mb][r] *= alpha;
-        m_run[qb] = m_new;
+          for (int r = 0; r < 16; ++r) oacc[mb][r] *= alpha;
+        m_run = m_new;
       }
-      const float mc = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb] * c;
+      const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
+      bf16x8 pop[2];
       float psum = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][r], c, -mc));
-        pop[qb][r >> 3][r & 7] = static_cast<__bf16>(pv);
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -mc));
+        pop[r >> 3][r & 7] = static_cast<__bf16>(pv);
         psum += pv;
       }
-      l_run[qb] += psum;
-    }
+      l_run += psum;
 
-    // O^T += V^T P^T over the stage's two 16-key chunks
+      // O^T += V^T P^T over the stage's two 16-key chunks
 #pragma unroll
-    for (int cc = 0; cc < SK / 16; ++cc) {
+      for (int cc = 0; cc < SK / 16; ++cc) {
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4_t*)(lb + TILE_B + mb * GB + vaddr[0] + cc * 16 * 64));
-        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4_t*)(lb + TILE_B + mb * GB + vaddr[1] + cc * 16 * 64));
-        const i16x8 vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-        bf16x8 vop;
-        __builtin_memcpy(&vop, &vv, 16);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) oacc[qb][mb] = mfma32(vop, pop[qb][cc], oacc[qb][mb]);
+        for (int mb = 0; mb < MB; ++mb) {
+          const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4_t*)(lb + TILE_B + mb * GB + vaddr[0] + cc * 16 * 64));
+          const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4_t*)(lb + TILE_B + mb * GB + vaddr[1] + cc * 16 * 64));
+          const i16x8 vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+          bf16x8 vop;
+          __builtin_memcpy(&vop, &vv, 16);
+          oacc[mb] = mfma32(vop, pop[cc], oacc[mb]);
+        }
       }
     }
     wait_dma();
@@ -222,45 +210,41 @@ void ffa_fwd_kernel(FwdArgs a) {
   // LSE = ln(e^LSE_1 + e^LSE_2), O = e^(LSE_1-LSE) O_1 + e^(LSE_2-LSE) O_2;
   // a row without valid keys in this call keeps its stored values.
   const bool acc = (a.flags & FFA_ACCUMULATE) != 0;
+  const float l_tot = wave_swap_sum(l_run);
+  if (row0 < a.Tq) {
+    float lse_new = l_tot > 0.f ? m_run * a.scale + logf(l_tot) : -INFINITY;
+    float w_new = l_tot > 0.f ? 1.f / l_tot : 0.f, w_old = 0.f;
+    bool write = true;
+    float* lp = a.lse + (int64_t)head * a.Tq + row0;
+    if (acc) {
+      const float lse_old = *lp;
+      if (lse_new == -INFINITY) {
+        write = false;
+      } else if (lse_old != -INFINITY) {
+        const float mx = fmaxf(lse_old, lse_new);
+        const float e1 = expf(lse_old - mx), e2 = expf(lse_new - mx);
+        const float den = e1 + e2;
+        lse_new = mx + logf(den);
+        w_old = e1 / den;
+        w_new *= e2 / den;
+      }
+    }
+    if (write) {
+      __bf16* op = a.o + (int64_t)row0 * a.o_ts + (int64_t)head * a.o_hs;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qrow = row0 + 32 * qb;
-    const float l_tot = wave_swap_sum(l_run[qb]);
-    if (qrow < a.Tq) {
-      float lse_new = l_tot > 0.f ? m_run[qb] * a.scale + logf(l_tot) : -INFINITY;
-      float w_new = l_tot > 0.f ? 1.f / l_tot : 0.f, w_old = 0.f;
-      bool write = true;
-      float* lp = a.lse + (int64_t)head * a.Tq + qrow;
-      if (acc) {
-        const float lse_old = *lp;
-        if (lse_new == -INFINITY) {
-          write = false;
-        } else if (lse_old != -INFINITY) {
-          const float mx = fmaxf(lse_old, lse_new);
-          const float e1 = expf(lse_old - mx), e2 = expf(lse_new - mx);
-          const float den = e1 + e2;
-          lse_new = mx + logf(den);
-          w_old = e1 / den;
-          w_new *= e2 / den;
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          bf16x4* dst = reinterpret_cast<bf16x4*>(op + 32 * mb + 8 * j + 4 * h32);
+          bf16x4 old = bf16x4{};
+          if (w_old != 0.f) old = *dst;
+          bf16x4 w;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            w[i] = static_cast<__bf16>(oacc[mb][4 * j + i] * w_new + static_cast<float>(old[i]) * w_old);
+          *dst = w;
         }
-      }
-      if (write) {
-        __bf16* op = a.o + (int64_t)qrow * a.o_ts + (int64_t)head * a.o_hs;
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            bf16x4* dst = reinterpret_cast<bf16x4*>(op + 32 * mb + 8 * j + 4 * h32);
-            bf16x4 old = bf16x4{};
-            if (w_old != 0.f) old = *dst;
-            bf16x4 w;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              w[i] = static_cast<__bf16>(oacc[qb][mb][4 * j + i] * w_new + static_cast<float>(old[i]) * w_old);
-            *dst = w;
-          }
-        if (h32 == 0) *lp = lse_new;
-      }
+      if (h32 == 0) *lp = lse_new;
     }
   }
 }
