@@ -103,13 +103,14 @@ __global__ void meta_init_kernel(const int32_t* __restrict__ slices, void* meta,
 }
 
 // Per-slice bounds / type checks and pairwise disjointness, one thread per
-// ordered pair (a <= b).  Two slices overlap iff some shared row has
-// intersecting key intervals.
-__global__ void meta_validate_kernel(void* meta) {
+// ordered pair (a <= b) of a 16 x 16 tile of pairs.  Two slices overlap iff
+// some shared row has intersecting key intervals.
+__device__ void validate_tile(void* meta, int tile) {
   MetaPtrs p = meta_ptrs(meta);
   const int S = p.hdr->num_slices, Tq = p.hdr->seqlen_q, Tk = p.hdr->seqlen_k;
-  const int a = blockIdx.y * 16 + threadIdx.y;
-  const int b = blockIdx.x * 16 + threadIdx.x;
+  const int nt = (S + 15) / 16;
+  const int a = (tile / nt) * 16 + (threadIdx.x >> 4);
+  const int b = (tile % nt) * 16 + (threadIdx.x & 15);
   if (a >= S || b >= S || b < a) return;
   const Slice sa = load_slice(p.slices, a);
   if (a == b) {
@@ -163,18 +164,26 @@ __device__ int block_exclusive_scan(int x, int* lds_ws, int* total) {
 // One owner block of the q2k (DIR = 0) or k2q (DIR = 1) classification.
 // FILL = false: write the Full / Partial counts of the owner (and, for q2k,
 // its slice count and area).  FILL = true: write the ascending index lists.
+struct TilesLds {
+  int cnt[CH];
+  int diff[CH + 1];
+  int slist[MT];
+  int ws[MT / 64 + 1];
+  int minmax[2];
+  long long area[MT / 64];
+};
+
 template <int DIR, bool FILL>
-__global__ __launch_bounds__(MT) void meta_tiles_kernel(void* meta) {
-  __shared__ int cnt[CH];
-  __shared__ int diff[CH + 1];
-  __shared__ int slist[MT];
-  __shared__ int ws[MT / 64 + 1];
-  __shared__ int sh_minmax[2];
+__device__ void tiles_block(void* meta, int own, TilesLds& sm) {
+  int* const cnt = sm.cnt;
+  int* const diff = sm.diff;
+  int* const slist = sm.slist;
+  int* const ws = sm.ws;
+  int* const sh_minmax = sm.minmax;
 
   MetaPtrs p = meta_ptrs(meta);
   const MetaHeader* h = p.hdr;
   const int S = h->num_slices, Tq = h->seqlen_q, Tk = h->seqlen_k;
-  const int own = blockIdx.x;
   // owner axis A and iterated axis B
   const int BA = DIR == 0 ? BM_F : BN_B;
   const int BB = DIR == 0 ? BN_F : BM_B;
@@ -329,7 +338,7 @@ __global__ __launch_bounds__(MT) void meta_tiles_kernel(void* meta) {
     }
     if (DIR == 0) {
       // block-reduce the area (int64) and add once per owner
-      __shared__ long long sarea[MT / 64];
+      long long* const sarea = sm.area;
       long long x = area;
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
@@ -407,15 +416,15 @@ __global__ void meta_scan_kernel(void* meta) {
 // MAX_SORT keep their natural order.
 constexpr int MAX_SORT = 32768;
 
-__global__ void meta_schedule_kernel(void* meta) {
+__device__ void schedule_block(void* meta, int which, int blk) {
   MetaPtrs p = meta_ptrs(meta);
   const MetaHeader* h = p.hdr;
-  const int which = blockIdx.y;   // 0: fwd q-blocks, 1: bwd k-blocks
+  // which = 0: fwd q-blocks, 1: bwd k-blocks
   const int n = which == 0 ? h->nq_f : h->nk_b;
   const int32_t* fo = which == 0 ? p.qf_off : p.kf_off;
   const int32_t* mo = which == 0 ? p.qm_off : p.km_off;
   int32_t* out = which == 0 ? p.sched_f : p.sched_b;
-  const int o = blockIdx.x * blockDim.x + threadIdx.x;
+  const int o = blk * MT + threadIdx.x;
   if (o >= n) return;
   if (n > MAX_SORT) {
     out[o] = o;
@@ -429,6 +438,27 @@ __global__ void meta_schedule_kernel(void* meta) {
     rank += (cx > c) || (cx == c && x < o);
   }
   out[rank] = o;
+}
+
+// Counting launch: blocks [0, nq_f) count q2k owners, the next nk_b count k2q
+// owners, the rest validate 16 x 16 tiles of slice pairs.
+__global__ __launch_bounds__(MT) void meta_count_kernel(void* meta, int nq, int nk) {
+  __shared__ TilesLds sm;
+  const int b = blockIdx.x;
+  if (b < nq) tiles_block<0, false>(meta, b, sm);
+  else if (b < nq + nk) tiles_block<1, false>(meta, b - nq, sm);
+  else validate_tile(meta, b - nq - nk);
+}
+
+// Filling launch: blocks [0, nq_f) fill q2k lists, the next nk_b fill k2q
+// lists, the rest rank owners for the longest-first schedules (ns blocks per
+// direction).
+__global__ __launch_bounds__(MT) void meta_fill_kernel(void* meta, int nq, int nk, int ns) {
+  __shared__ TilesLds sm;
+  const int b = blockIdx.x;
+  if (b < nq) tiles_block<0, true>(meta, b, sm);
+  else if (b < nq + nk) tiles_block<1, true>(meta, b - nq, sm);
+  else schedule_block(meta, (b - nq - nk) / ns, (b - nq - nk) % ns);
 }
 
 }  // namespace
@@ -449,18 +479,15 @@ hipError_t launch_build_meta(const int32_t* d_slices, int32_t S, int32_t Tq, int
   for (int i = 0; i < 9; ++i) ia.byte_off[i] = L.byte_off[i];
   const int n5 = 5 * S;
   const int gi = n5 > 0 ? min(1024, (n5 + 255) / 256) : 1;
+  // four launches: init | validate + count | scan | fill + schedule
   meta_init_kernel<<<gi, 256, 0, stream>>>(d_slices, d_meta, ia);
-  if (S > 0) {
-    dim3 g((S + 15) / 16, (S + 15) / 16);
-    meta_validate_kernel<<<g, dim3(16, 16), 0, stream>>>(d_meta);
-  }
-  if (L.nq_f > 0) meta_tiles_kernel<0, false><<<L.nq_f, MT, 0, stream>>>(d_meta);
-  if (L.nk_b > 0) meta_tiles_kernel<1, false><<<L.nk_b, MT, 0, stream>>>(d_meta);
+  const int nv = S > 0 ? ((S + 15) / 16) * ((S + 15) / 16) : 0;
+  if (L.nq_f + L.nk_b + nv > 0)
+    meta_count_kernel<<<L.nq_f + L.nk_b + nv, MT, 0, stream>>>(d_meta, L.nq_f, L.nk_b);
   meta_scan_kernel<<<1, 1024, 0, stream>>>(d_meta);
-  if (L.nq_f > 0) meta_tiles_kernel<0, true><<<L.nq_f, MT, 0, stream>>>(d_meta);
-  if (L.nk_b > 0) meta_tiles_kernel<1, true><<<L.nk_b, MT, 0, stream>>>(d_meta);
-  const int nmax = max(L.nq_f, L.nk_b);
-  if (nmax > 0) meta_schedule_kernel<<<dim3((nmax + 255) / 256, 2), 256, 0, stream>>>(d_meta);
+  const int ns = (max(L.nq_f, L.nk_b) + MT - 1) / MT;
+  if (L.nq_f + L.nk_b + 2 * ns > 0)
+    meta_fill_kernel<<<L.nq_f + L.nk_b + 2 * ns, MT, 0, stream>>>(d_meta, L.nq_f, L.nk_b, ns);
   return hipGetLastError();
 }
 
