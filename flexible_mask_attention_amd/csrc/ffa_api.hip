@@ -1,6 +1,7 @@
 // ffa_api.hip - host side of the libffa C ABI: argument validation, metadata
 // layout and kernel dispatch.  Nothing here allocates, synchronises or keeps
 // state; every call only enqueues kernels on the caller's stream.
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -50,6 +51,47 @@ ffa_status check_shape(const ffa_shape* s) {
   if (s->head_dim != 64 && s->head_dim != 128) return FFA_ERR_UNSUPPORTED;
   if (!std::isfinite(s->softmax_scale) || !(s->softmax_scale > 0.f)) return FFA_ERR_INVALID_ARGUMENT;
   return FFA_OK;
+}
+
+}  // namespace
+
+namespace {
+
+// Backward workspace: -D and LSE log2 e rows, then the split counters and the
+// split partial sums of the dK/dV kernel, each 256-byte aligned.
+struct BwdWsLayout {
+  int64_t lvec, cnt, part, total;
+  int32_t split_e;
+};
+
+BwdWsLayout bwd_ws_layout(const ffa_shape& s) {
+  BwdWsLayout W;
+  const int64_t rows = align256(4LL * s.num_heads_q * s.seqlen_q);
+  const int32_t nk_b = cdiv(s.seqlen_k, BN_B);
+  W.split_e = split_candidates(s.num_heads_kv, nk_b);
+  const int64_t nc = (int64_t)W.split_e * s.num_heads_kv;
+  W.lvec = rows;
+  W.cnt = 2 * rows;
+  W.part = W.cnt + align256(4 * nc);
+  W.total = W.part + nc * 2 * 2 * BN_B * (int64_t)s.head_dim * 4;
+  return W;
+}
+
+// dK/dV workgroups resident at once on the current device (two per compute
+// unit), cached per device.
+int resident_dkdv_slots() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return 0;
+  if (dev >= 0 && dev < 64) cache[dev].store(2 * cus, std::memory_order_relaxed);
+  return 2 * cus;
 }
 
 }  // namespace
@@ -180,7 +222,7 @@ FFA_API ffa_status ffa_bwd_workspace_size(const ffa_shape* shape, size_t* bytes)
   ffa_status st = check_shape(shape);
   if (st != FFA_OK) return st;
   if (!bytes) return FFA_ERR_INVALID_ARGUMENT;
-  *bytes = (size_t)(2 * align256(4LL * shape->num_heads_q * shape->seqlen_q));
+  *bytes = (size_t)bwd_ws_layout(*shape).total;
   return FFA_OK;
 }
 
@@ -237,9 +279,18 @@ FFA_API ffa_status ffa_bwd_ex(const ffa_shape* shape, ffa_tensor_in q, ffa_tenso
   a.o = static_cast<const __bf16*>(o.ptr);
   a.dout = static_cast<const __bf16*>(dout.ptr);
   a.lse = lse;
-  a.dvec = static_cast<float*>(d_ws);
-  a.lvec = reinterpret_cast<float*>(static_cast<char*>(d_ws) +
-                                    align256(4LL * shape->num_heads_q * shape->seqlen_q));
+  const BwdWsLayout W = bwd_ws_layout(*shape);
+  char* ws = static_cast<char*>(d_ws);
+  a.dvec = reinterpret_cast<float*>(ws);
+  a.lvec = reinterpret_cast<float*>(ws + W.lvec);
+  a.split_cnt = reinterpret_cast<int32_t*>(ws + W.cnt);
+  a.split_part = reinterpret_cast<float*>(ws + W.part);
+  a.split_e = W.split_e;
+  a.split_slots = 0;
+  if (W.split_e > 0) {
+    a.split_slots = resident_dkdv_slots();
+    if (a.split_slots <= 0) return FFA_ERR_HIP;
+  }
   a.dq = static_cast<__bf16*>(dq.ptr);
   a.dk = static_cast<__bf16*>(dk.ptr);
   a.dv = static_cast<__bf16*>(dv.ptr);

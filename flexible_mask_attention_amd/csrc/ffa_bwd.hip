@@ -99,6 +99,12 @@ __global__ __launch_bounds__(NT, 3) __attribute__((amdgpu_waves_per_eu(3, 3))) v
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h32 = lane >> 5, t16 = lane & 15, g16 = lane >> 4;
+  if constexpr (PRE) {
+    // the dK/dV kernel that follows in this stream expects its split
+    // counters at zero
+    if (blockIdx.x == 0)
+      for (int i = tid; i < a.split_e * a.Hkv; i += NT) a.split_cnt[i] = 0;
+  }
   int item, head;
   xcd_map(blockIdx.x, a.Hq, item, head);
   const int m = mv.sched_f[item];
@@ -309,7 +315,6 @@ __global__ __launch_bounds__(NT, 3) __attribute__((amdgpu_waves_per_eu(3, 3))) v
 hipError_t launch_bwd(const BwdArgs& a, int head_dim, int nq_f, int nk_b, int phases,
                       hipStream_t stream) {
   const int64_t rows = (int64_t)a.Tq * a.Hq;
-  const int64_t gk = (int64_t)nk_b * a.Hkv;
   const int64_t gq = (int64_t)nq_f * a.Hq;
   // PRE together with DQ: the dQ kernel computes the row statistics itself and
   // runs first; otherwise PRE is its own kernel.
@@ -325,8 +330,8 @@ hipError_t launch_bwd(const BwdArgs& a, int head_dim, int nq_f, int nk_b, int ph
     if (head_dim == 128) ffa_bwd_pre_kernel<128><<<dim3((unsigned)blocks), NT, 0, stream>>>(a);
     else ffa_bwd_pre_kernel<64><<<dim3((unsigned)blocks), NT, 0, stream>>>(a);
   }
-  if ((phases & FFA_BWD_DKDV) && gk > 0) {
-    const hipError_t e = launch_bwd_dkdv(a, head_dim, gk, stream);
+  if ((phases & FFA_BWD_DKDV) && nk_b > 0 && a.Hkv > 0) {
+    const hipError_t e = launch_bwd_dkdv(a, head_dim, nk_b, fused, stream);
     if (e != hipSuccess) return e;
   }
   if (!fused && (phases & FFA_BWD_DQ) && gq > 0) {

@@ -2,7 +2,8 @@
 //
 // Owner (kv head, 128-key block); loops over the query heads that share the kv
 // head and the k2q tiles of the block, in a fixed order, so dK and dV are
-// bitwise reproducible without atomics (the backward of the MagiAttention
+// bitwise reproducible (the few longest blocks are done as two halves whose
+// fp32 sums are added once, see below) (the backward of the MagiAttention
 // pages' FFA kernel, blog deep-dive, section "Flex-Flash-Attention 与
 // AttnSlice", Fig. 5, written with one owner per output):
 //   S = Q K^T, P = exp(S - LSE) (masked on Partial tiles), dV += P^T dO,
@@ -43,7 +44,18 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   const int l32 = lane & 31, h32 = lane >> 5, t16 = lane & 15, g16 = lane >> 4;
   int item, kvh;
   xcd_map(blockIdx.x, a.Hkv, item, kvh);
-  const int n = mv.sched_b[item];
+  // Items [0, 2 split_e) are the two halves of the split_e longest blocks (the
+  // schedule is longest first); a candidate is split only if its work exceeds
+  // what one resident workgroup would get with the whole backward spread
+  // evenly, cost * slots > Hkv * total cost (the query heads per kv head
+  // cancel), otherwise its first item does all of it and the second exits.
+  int part = -1, cand = 0, n;
+  if (item < 2 * a.split_e) {
+    cand = item >> 1;
+    n = mv.sched_b[cand];
+  } else {
+    n = mv.sched_b[item - a.split_e];
+  }
   const int key = n * BN_B + wid * 32 + l32;
   const bool kok = key < a.Tk;
   const int G = a.Hq / a.Hkv;
@@ -51,6 +63,12 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   const int f0 = mv.kf_off[n], nF = mv.kf_off[n + 1] - f0;
   const int p0 = mv.km_off[n], nP = mv.km_off[n + 1] - p0;
   const int nT = nP + nF;
+  if (item < 2 * a.split_e) {
+    const int64_t cost = 4LL * nF + 5LL * nP;
+    const int64_t tot = 4LL * hd->nnz[L_KF] + 5LL * hd->nnz[L_KM];
+    if (cost * a.split_slots > tot * a.Hkv && G * nT >= 4) part = item & 1;
+    else if (item & 1) return;
+  }
   cint32_t* fidx = mv.var + hd->list_off[L_KF] + f0;
   cint32_t* pidx = mv.var + hd->list_off[L_KM] + p0;
 
@@ -99,6 +117,9 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   // sequence starts at the sequence's last query tile and the blocks resident
   // on one XCD move through the same Q / dO tiles at about the same time.
   const int total = G * nT;
+  // this workgroup's steps: all of them, or one half of a split block
+  const int ubeg = part == 1 ? total / 2 : 0;
+  const int uend = part == 0 ? total / 2 : total;
   auto tile_of = [&](int t) { return t < nP ? pidx[t] : fidx[t - nP]; };
   auto issue = [&](int u, int stage) {
     const int hq = kvh * G + u % G;
@@ -121,7 +142,7 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     const int t = nT - 1 - u / G;
     const bool masked = t < nP;
     const int m = tile_of(t);
-    if (u + 1 < total) issue(u + 1, stage ^ 1);
+    if (u + 1 < uend) issue(u + 1, stage ^ 1);
     const __attribute__((address_space(3))) char* lb =
         (const __attribute__((address_space(3))) char*)smem + stage * STAGE_B;
 
@@ -221,12 +242,55 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     __syncthreads();
   };
 
-  if (total > 0) issue(0, 0);
+  if (ubeg < uend) issue(ubeg, 0);
   wait_dma();
   __syncthreads();
-  for (int u = 0; u < total; u += 2) {
+  for (int u = ubeg; u < uend; u += 2) {
     tile(std::integral_constant<int, 0>{}, u);
-    if (u + 1 < total) tile(std::integral_constant<int, 1>{}, u + 1);
+    if (u + 1 < uend) tile(std::integral_constant<int, 1>{}, u + 1);
+  }
+
+  if (part >= 0) {
+    // Both halves store their fp32 partial sums, then count themselves in;
+    // the second one adds the other half's partial to its own and writes the
+    // result.  One fp32 addition of two terms is commutative, so the result
+    // does not depend on which half finishes last.  Partials are stored in
+    // register order (per (mb, j), 16 bytes per lane, a wave's 64 lanes
+    // contiguous), which only this kernel reads.
+    float* slot = a.split_part + ((int64_t)cand * a.Hkv + kvh) * (2 * 2 * BN_B * D);
+    float* mine = slot + part * (2 * BN_B * D);
+    const float* other = slot + (1 - part) * (2 * BN_B * D);
+    const int lofs = (wid * 64 + lane) * 4;
+    auto at = [&](int mb, int j) { return (mb * 4 + j) * (BN_B * 8) + lofs; };
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 k4 = {dkacc[mb][4 * j], dkacc[mb][4 * j + 1], dkacc[mb][4 * j + 2], dkacc[mb][4 * j + 3]};
+        const f32x4 v4 = {dvacc[mb][4 * j], dvacc[mb][4 * j + 1], dvacc[mb][4 * j + 2], dvacc[mb][4 * j + 3]};
+        *reinterpret_cast<f32x4*>(mine + at(mb, j)) = k4;
+        *reinterpret_cast<f32x4*>(mine + BN_B * D + at(mb, j)) = v4;
+      }
+    __threadfence();
+    __syncthreads();
+    int* flag = reinterpret_cast<int*>(smem);   // the tile ring is idle now
+    if (tid == 0) *flag = atomicAdd(a.split_cnt + (int64_t)cand * a.Hkv + kvh, 1);
+    __syncthreads();
+    if (*flag == 0) return;   // the other half finishes the block
+    __threadfence();
+    if (tid == 0) a.split_cnt[(int64_t)cand * a.Hkv + kvh] = 0;   // ready for the next launch
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 k4 = *reinterpret_cast<const f32x4*>(other + at(mb, j));
+        const f32x4 v4 = *reinterpret_cast<const f32x4*>(other + BN_B * D + at(mb, j));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          dkacc[mb][4 * j + i] += k4[i];
+          dvacc[mb][4 * j + i] += v4[i];
+        }
+      }
   }
 
   if (kok) {
@@ -257,9 +321,19 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   }
 }
 
+__global__ __launch_bounds__(NT) void split_clear_kernel(int32_t* cnt, int n) {
+  for (int i = blockIdx.x * NT + threadIdx.x; i < n; i += gridDim.x * NT) cnt[i] = 0;
+}
+
 }  // namespace
 
-hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int64_t grid, hipStream_t stream) {
+hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int nk_b, bool counters_clear,
+                           hipStream_t stream) {
+  const int64_t grid = (int64_t)(nk_b + a.split_e) * a.Hkv;
+  if (grid == 0) return hipSuccess;
+  const int ncnt = a.split_e * a.Hkv;
+  if (ncnt > 0 && !counters_clear)
+    split_clear_kernel<<<dim3((unsigned)((ncnt + NT - 1) / NT)), NT, 0, stream>>>(a.split_cnt, ncnt);
   if (head_dim == 128) {
     const size_t lds = 2 * (2 * BM_B * 128 * 2 + 2 * BM_B * 4);
     ffa_bwd_dkdv_kernel<128><<<dim3((unsigned)grid), NT, lds, stream>>>(a);

@@ -364,9 +364,30 @@ struct BwdArgs {
   float scale_log2;
   float scale;
   uint32_t flags;     // FFA_ACCUMULATE: add to the dq / dk / dv already in the buffers
+  // Split key blocks (dK / dV load balance): the split_e longest key blocks of
+  // each kv head may be done as two halves of their query-tile walk by two
+  // workgroups; the second to finish adds the other's fp32 partial.
+  int32_t* split_cnt;   // workspace: [split_e][Hkv] finish counters, zero between launches
+  float* split_part;    // workspace: [split_e][Hkv][2 halves][dK, dV][BN_B * D] fp32
+  int32_t split_e;      // candidate blocks per kv head (<= nk_b)
+  int32_t split_slots;  // dK/dV workgroups resident on the device at once
 };
+
+// Number of split candidates per kv head: enough for the long blocks of a
+// causal varlen batch on one XCD, bounded so the partial buffers stay about
+// 32 MB for d = 128 whatever Hkv is.
+__host__ __device__ inline int32_t split_candidates(int32_t Hkv, int32_t nk_b) {
+  int32_t e = Hkv > 0 ? 128 / Hkv : 0;
+  e = e < 4 ? 4 : (e > 32 ? 32 : e);
+  return e < nk_b ? e : nk_b;
+}
+
 hipError_t launch_bwd(const BwdArgs& a, int head_dim, int nq_f, int nk_b, int phases,
                       hipStream_t stream);
-hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int64_t grid, hipStream_t stream);
+// counters_clear: the split counters were already zeroed in this stream (by
+// the dQ kernel that computes the row statistics); otherwise a small kernel
+// clears them first.
+hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int nk_b, bool counters_clear,
+                           hipStream_t stream);
 
 }  // namespace ffa

@@ -167,13 +167,20 @@ FFA_API ffa_status ffa_fwd(const ffa_shape* shape, ffa_tensor_in q, ffa_tensor_i
                            void* stream);
 
 /* Scratch bytes ffa_bwd needs: per (query head, row) the dot product
- * -D_i = -(dO_i . O_i) and LSE_i * log2(e), both fp32. */
+ * -D_i = -(dO_i . O_i) and LSE_i * log2(e), both fp32; then, for the dK/dV
+ * load balance, finish counters and fp32 partial dK, dV of the longest key
+ * blocks of each kv head (up to min(32, max(4, 128 / num_heads_kv)) blocks of
+ * 128 keys, two halves each).  Depends on the shape only. */
 FFA_API ffa_status ffa_bwd_workspace_size(const ffa_shape* shape, size_t* bytes);
 
 /* Backward: dq, dk, dv of the forward above, given its o and lse.
  * dk and dv are accumulated per key block in a fixed order over the k2q tiles
  * and the query heads that share the key head, and dq per query block over
- * its q2k tiles, so results are bitwise reproducible (no atomics).
+ * its q2k tiles.  A key block whose work exceeds an even share of the
+ * device's resident workgroups is done as two halves of that order whose fp32
+ * sums are added once (a commutative step), so results are bitwise
+ * reproducible on a given device; the split choice depends on the number of
+ * compute units.  Calls that share one workspace must not run concurrently.
  * d_ws: device scratch of at least ffa_bwd_workspace_size bytes, 256-byte aligned. */
 FFA_API ffa_status ffa_bwd(const ffa_shape* shape, ffa_tensor_in q, ffa_tensor_in k,
                            ffa_tensor_in v, ffa_tensor_in o, const float* lse,
