@@ -80,7 +80,8 @@ constexpr size_t dq_lds_bytes() {
 // for the dK/dV kernel, which then runs after this one.
 template <int D, bool PRE>
 __global__ __launch_bounds__(NT, 3) __attribute__((amdgpu_waves_per_eu(3, 3))) void ffa_bwd_dq_kernel(BwdArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+  // statically sized: a known LDS address lets operand reads use immediates
+  __shared__ __attribute__((aligned(16))) char smem[dq_lds_bytes<D>()];
   constexpr int SK = DQ_SK;
   constexpr int TILE_B = SK * D * 2;            // one K or V stage tile
   constexpr int STAGE_B = 2 * TILE_B;
@@ -321,9 +322,9 @@ hipError_t launch_bwd(const BwdArgs& a, int head_dim, int nq_f, int nk_b, int ph
   const bool fused = (phases & FFA_BWD_PRE) && (phases & FFA_BWD_DQ) && gq > 0;
   if (fused) {
     if (head_dim == 128)
-      ffa_bwd_dq_kernel<128, true><<<dim3((unsigned)gq), NT, dq_lds_bytes<128>(), stream>>>(a);
+      ffa_bwd_dq_kernel<128, true><<<dim3((unsigned)gq), NT, 0, stream>>>(a);
     else
-      ffa_bwd_dq_kernel<64, true><<<dim3((unsigned)gq), NT, dq_lds_bytes<64>(), stream>>>(a);
+      ffa_bwd_dq_kernel<64, true><<<dim3((unsigned)gq), NT, 0, stream>>>(a);
   } else if ((phases & FFA_BWD_PRE) && rows > 0) {
     const int G = head_dim / 8;
     const int64_t blocks = (rows * G + NT - 1) / NT;
@@ -336,9 +337,9 @@ hipError_t launch_bwd(const BwdArgs& a, int head_dim, int nq_f, int nk_b, int ph
   }
   if (!fused && (phases & FFA_BWD_DQ) && gq > 0) {
     if (head_dim == 128)
-      ffa_bwd_dq_kernel<128, false><<<dim3((unsigned)gq), NT, dq_lds_bytes<128>(), stream>>>(a);
+      ffa_bwd_dq_kernel<128, false><<<dim3((unsigned)gq), NT, 0, stream>>>(a);
     else
-      ffa_bwd_dq_kernel<64, false><<<dim3((unsigned)gq), NT, dq_lds_bytes<64>(), stream>>>(a);
+      ffa_bwd_dq_kernel<64, false><<<dim3((unsigned)gq), NT, 0, stream>>>(a);
   }
   return hipGetLastError();
 }

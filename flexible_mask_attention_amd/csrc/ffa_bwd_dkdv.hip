@@ -28,9 +28,10 @@ constexpr int NT = 256;
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void ffa_bwd_dkdv_kernel(BwdArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int TILE_B = BM_B * D * 2;          // bytes of one Q or dO tile
   constexpr int STAGE_B = 2 * TILE_B + 2 * BM_B * 4;
+  // statically sized: a known LDS address lets operand reads use immediates
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE_B];
   constexpr int QB = BM_B / 32;                 // 32-row query blocks per tile
   constexpr int MB = D / 32;
   constexpr int KS = D / 16;
@@ -334,13 +335,8 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int nk_b, bool counte
   const int ncnt = a.split_e * a.Hkv;
   if (ncnt > 0 && !counters_clear)
     split_clear_kernel<<<dim3((unsigned)((ncnt + NT - 1) / NT)), NT, 0, stream>>>(a.split_cnt, ncnt);
-  if (head_dim == 128) {
-    const size_t lds = 2 * (2 * BM_B * 128 * 2 + 2 * BM_B * 4);
-    ffa_bwd_dkdv_kernel<128><<<dim3((unsigned)grid), NT, lds, stream>>>(a);
-  } else {
-    const size_t lds = 2 * (2 * BM_B * 64 * 2 + 2 * BM_B * 4);
-    ffa_bwd_dkdv_kernel<64><<<dim3((unsigned)grid), NT, lds, stream>>>(a);
-  }
+  if (head_dim == 128) ffa_bwd_dkdv_kernel<128><<<dim3((unsigned)grid), NT, 0, stream>>>(a);
+  else ffa_bwd_dkdv_kernel<64><<<dim3((unsigned)grid), NT, 0, stream>>>(a);
   return hipGetLastError();
 }
 

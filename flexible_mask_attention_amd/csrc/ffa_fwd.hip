@@ -36,9 +36,11 @@ static_assert(RW == 32 && BN_F % SK == 0 && 2 * SK == 16 * NW, "forward tiling")
 template <int D>
 __global__ __launch_bounds__(NT, 3) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void ffa_fwd_kernel(FwdArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int TILE_B = SK * D * 2;            // bytes of one K or V stage tile
   constexpr int STAGE_B = 2 * TILE_B;
+  // statically sized, so its LDS address is a known constant and the operand
+  // read addresses fold into immediate offsets
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE_B];
   constexpr int MB = D / 32;                    // 32-wide d blocks of O^T
   constexpr int KS = D / 16;                    // 16-wide d steps of S^T
   constexpr int GB = group_bytes<SK>();
@@ -254,13 +256,8 @@ void ffa_fwd_kernel(FwdArgs a) {
 hipError_t launch_fwd(const FwdArgs& a, int head_dim, int nq_f, hipStream_t stream) {
   const int64_t grid = (int64_t)nq_f * a.Hq;
   if (grid == 0) return hipSuccess;
-  if (head_dim == 128) {
-    const size_t lds = 2 * 2 * SK * 128 * 2;
-    ffa_fwd_kernel<128><<<dim3((unsigned)grid), NT, lds, stream>>>(a);
-  } else {
-    const size_t lds = 2 * 2 * SK * 64 * 2;
-    ffa_fwd_kernel<64><<<dim3((unsigned)grid), NT, lds, stream>>>(a);
-  }
+  if (head_dim == 128) ffa_fwd_kernel<128><<<dim3((unsigned)grid), NT, 0, stream>>>(a);
+  else ffa_fwd_kernel<64><<<dim3((unsigned)grid), NT, 0, stream>>>(a);
   return hipGetLastError();
 }
 
