@@ -16,6 +16,7 @@ import math
 import os
 from typing import Optional, Sequence
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -27,7 +28,7 @@ META_ERR_BOUNDS, META_ERR_TYPE, META_ERR_OVERLAP, META_ERR_CAPACITY = 1, 2, 4, 8
 EXPORTED = (
     "ffa_block_meta_workspace_size", "ffa_build_block_meta", "ffa_block_meta_view", "ffa_fwd",
     "ffa_bwd_workspace_size", "ffa_bwd", "ffa_bwd_phases", "ffa_status_string", "ffa_abi_version",
-    "ffa_fwd_ex", "ffa_bwd_ex",
+    "ffa_fwd_ex", "ffa_bwd_ex", "ffa_chunk_areas", "ffa_dispatch_chunks", "ffa_rank_slices",
 )
 BWD_PRE, BWD_DKDV, BWD_DQ, BWD_ALL = 1, 2, 4, 7
 ACCUMULATE = 1                  # FFA_ACCUMULATE flag of ffa_fwd_ex / ffa_bwd_ex
@@ -94,6 +95,13 @@ def lib() -> ctypes.CDLL:
     L.ffa_fwd_ex.restype = st
     L.ffa_bwd_ex.argtypes = L.ffa_bwd.argtypes[:-1] + [i32, ctypes.c_uint32, vp]
     L.ffa_bwd_ex.restype = st
+    P32, P64 = ctypes.POINTER(i32), ctypes.POINTER(i64)
+    L.ffa_chunk_areas.argtypes = [vp, i32, i32, i32, i32, vp]
+    L.ffa_chunk_areas.restype = st
+    L.ffa_dispatch_chunks.argtypes = [vp, i32, i32, vp]
+    L.ffa_dispatch_chunks.restype = st
+    L.ffa_rank_slices.argtypes = [vp, i32, i32, i32, i32, vp, i32, vp, i32, P32, vp, i32, P32]
+    L.ffa_rank_slices.restype = st
     L.ffa_status_string.argtypes = [st]
     L.ffa_status_string.restype = ctypes.c_char_p
     L.ffa_abi_version.argtypes = []
@@ -249,6 +257,56 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, meta: BlockMeta, scal
     return out, lse
 
 
+# ------------------------------------------------------------------------
+# Context-parallel dispatch (host only; see ffa.h)
+# ------------------------------------------------------------------------
+
+def _host_slices(slices) -> np.ndarray:
+    a = np.ascontiguousarray(np.asarray(slices, dtype=np.int32).reshape(-1, 5))
+    return a
+
+
+def chunk_areas(slices, seqlen_q: int, seqlen_k: int, chunk_size: int) -> np.ndarray:
+    """Valid (query, key) pairs of each query chunk of ``chunk_size`` tokens."""
+    h = _host_slices(slices)
+    n = -(-seqlen_q // chunk_size) if chunk_size > 0 else 0
+    out = np.zeros(max(n, 1), dtype=np.int64)
+    _check(lib().ffa_chunk_areas(h.ctypes.data if len(h) else None, len(h), seqlen_q, seqlen_k,
+                                 chunk_size, out.ctypes.data), "ffa_chunk_areas")
+    return out[:n]
+
+
+def dispatch_chunks(areas, cp_size: int) -> np.ndarray:
+    """Bucket (rank) of every chunk: equal chunk counts, greedy min-max area."""
+    a = np.ascontiguousarray(np.asarray(areas, dtype=np.int64))
+    out = np.zeros(len(a), dtype=np.int32)
+    _check(lib().ffa_dispatch_chunks(a.ctypes.data, len(a), cp_size, out.ctypes.data),
+           "ffa_dispatch_chunks")
+    return out
+
+
+def rank_slices(slices, seqlen_q: int, seqlen_k: int, chunk_size: int, chunks):
+    """Local slice table of the share made of ``chunks`` (in that order) and the
+    global key ranges it needs: (local_slices [S', 5], kv_ranges [R, 3] =
+    (global_start, global_end, buffer_start), local seqlen_k)."""
+    h = _host_slices(slices)
+    c = np.ascontiguousarray(np.asarray(chunks, dtype=np.int32))
+    nl, nk = ctypes.c_int32(), ctypes.c_int32()
+    L = lib()
+    args = (h.ctypes.data if len(h) else None, len(h), seqlen_q, seqlen_k, chunk_size,
+            c.ctypes.data if len(c) else None, len(c))
+    code = L.ffa_rank_slices(*args, None, 0, ctypes.byref(nl), None, 0, ctypes.byref(nk))
+    if code not in (0, 3):
+        _check(code, "ffa_rank_slices")
+    loc = np.zeros((max(nl.value, 1), 5), dtype=np.int32)
+    kv = np.zeros((max(nk.value, 1), 3), dtype=np.int32)
+    _check(L.ffa_rank_slices(*args, loc.ctypes.data, nl.value, ctypes.byref(nl), kv.ctypes.data,
+                             nk.value, ctypes.byref(nk)), "ffa_rank_slices")
+    loc, kv = loc[: nl.value], kv[: nk.value]
+    tk = int(kv[-1, 2] + kv[-1, 1] - kv[-1, 0]) if len(kv) else 0
+    return loc, kv, tk
+
+
 def bwd_workspace_size(q, k, scale=None) -> int:
     n = ctypes.c_size_t()
     sh = _shape(q, k, scale)
@@ -301,5 +359,6 @@ def ffa_attention(q, k, v, meta: BlockMeta, scale: float = None) -> torch.Tensor
 
 
 __all__ = ["BWD_PRE", "BWD_DKDV", "BWD_DQ", "BWD_ALL", "ACCUMULATE", "build_meta", "fwd", "bwd", "ffa_attention", "FFAFunction", "BlockMeta", "lib",
-           "meta_workspace_size", "bwd_workspace_size", "FFAError", "FULL", "CAUSAL", "INV_CAUSAL",
+           "meta_workspace_size", "bwd_workspace_size", "chunk_areas", "dispatch_chunks",
+           "rank_slices", "FFAError", "FULL", "CAUSAL", "INV_CAUSAL",
            "BI_CAUSAL", "EXPORTED"]

@@ -17,7 +17,8 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libffa.so")
-SOURCES = ["ffa_api.hip", "ffa_meta.hip", "ffa_fwd.hip", "ffa_bwd.hip", "ffa_bwd_dkdv.hip"]
+SOURCES = ["ffa_api.hip", "ffa_meta.hip", "ffa_fwd.hip", "ffa_bwd.hip", "ffa_bwd_dkdv.hip",
+           "ffa_dispatch.hip"]
 ARCH = os.environ.get("FFA_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

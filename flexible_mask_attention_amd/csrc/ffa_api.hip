@@ -107,6 +107,7 @@ FFA_API const char* ffa_status_string(ffa_status s) {
     case FFA_ERR_UNSUPPORTED: return "unsupported configuration";
     case FFA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case FFA_ERR_HIP: return "HIP launch failed";
+    case FFA_ERR_BAD_SLICES: return "bad slice table";
   }
   return "unknown status";
 }

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define FFA_ABI_VERSION 2
+#define FFA_ABI_VERSION 3
 
 #if defined(__GNUC__)
 #define FFA_API __attribute__((visibility("default")))
@@ -69,7 +69,8 @@ typedef enum {
   FFA_ERR_INVALID_ARGUMENT = 1,    /* null/misaligned pointer, bad shape or stride */
   FFA_ERR_UNSUPPORTED = 2,         /* e.g. head_dim not 64 or 128 */
   FFA_ERR_WORKSPACE_TOO_SMALL = 3, /* meta_bytes or ws_bytes below the required size */
-  FFA_ERR_HIP = 4                  /* a kernel launch failed */
+  FFA_ERR_HIP = 4,                 /* a kernel launch failed */
+  FFA_ERR_BAD_SLICES = 5           /* host slice table: range out of bounds or unknown type */
 } ffa_status;
 
 /* Flags of the device status word inside the block metadata. */
@@ -238,6 +239,63 @@ FFA_API ffa_status ffa_bwd_ex(const ffa_shape* shape, ffa_tensor_in q, ffa_tenso
                               ffa_tensor_in dout, const void* d_meta, ffa_tensor_out dq,
                               ffa_tensor_out dk, ffa_tensor_out dv, void* d_ws, size_t ws_bytes,
                               int32_t phases, uint32_t flags, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Context-parallel dispatch (host only: no device memory, no stream).
+ *
+ * The query sequence is cut into n = ceil(seqlen_q / chunk_size) chunks; chunk c
+ * holds queries [c * chunk_size, min((c + 1) * chunk_size, seqlen_q)) and its
+ * area is the number of valid (query, key) pairs of those queries.  A dispatch
+ * puts the chunks into cp_size buckets (ranks) holding the same number of
+ * chunks each, aiming at the smallest largest bucket area, so that attention
+ * work is balanced while token-priced layers stay balanced too (MagiAttention
+ * blog deep-dive, section "Dispatch Solver": the chunk-count equation, the
+ * min-max objective with the equal-count constraint, and the greedy min-heap
+ * solution).
+ * ------------------------------------------------------------------------- */
+
+/* Area of every chunk.  host_slices: host int32 [num_slices][5], the table as
+ * for ffa_build_block_meta (bounds and types are checked here, disjointness is
+ * not: overlapping slices are counted once per slice).  areas: host int64
+ * [ceil(seqlen_q / chunk_size)].  chunk_size > 0.  A bad table gives
+ * FFA_ERR_BAD_SLICES and writes nothing. */
+FFA_API ffa_status ffa_chunk_areas(const int32_t* host_slices, int32_t num_slices,
+                                   int32_t seqlen_q, int32_t seqlen_k, int32_t chunk_size,
+                                   int64_t* areas);
+
+/* Greedy dispatch: the chunks, by decreasing area (equal areas: lower chunk
+ * index first), each go to the bucket with the least area so far among those
+ * still holding fewer than num_chunks / cp_size chunks (equal areas: lower
+ * bucket index).  bucket: host int32 [num_chunks], the bucket of each chunk.
+ * num_chunks must be a positive multiple of cp_size and areas >= 0.
+ * O(n log n) with a min-heap of buckets. */
+FFA_API ffa_status ffa_dispatch_chunks(const int64_t* areas, int32_t num_chunks,
+                                       int32_t cp_size, int32_t* bucket);
+
+/* The slice table of one rank's share.  chunks: host int32 [num_chunks],
+ * distinct chunk indices; the rank's local queries are these chunks
+ * concatenated in the given order.  Outputs (host int32):
+ *   local_slices [*][5]: slices over local query rows and receive-buffer key
+ *     columns with exactly the valid pairs of the global table on those
+ *     queries.  A slice cut to a sub-range [a, b) of its queries keeps its rule
+ *     by moving its key range: the end moves back by q_end - b for CAUSAL and
+ *     BI-CAUSAL, the start forward by a - q_start for INV-CAUSAL and
+ *     BI-CAUSAL; pieces without a valid pair are dropped.  Order: by position
+ *     of the chunk in `chunks`, then by slice index.
+ *   kv_ranges [*][3] = { global_start, global_end, buffer_start }: the sorted,
+ *     disjoint (and non-adjacent) global key ranges the local slices touch,
+ *     packed back to back in a receive buffer; the local seqlen_k is the end of
+ *     the last one.  These are the keys (and values) the rank has to fetch.
+ * max_local / max_kv are the capacities (in rows); num_local / num_kv receive
+ * the counts.  A short capacity gives FFA_ERR_WORKSPACE_TOO_SMALL with the
+ * needed counts written and the arrays untouched; a bad table
+ * FFA_ERR_BAD_SLICES; a chunk index out of range or repeated
+ * FFA_ERR_INVALID_ARGUMENT. */
+FFA_API ffa_status ffa_rank_slices(const int32_t* host_slices, int32_t num_slices,
+                                   int32_t seqlen_q, int32_t seqlen_k, int32_t chunk_size,
+                                   const int32_t* chunks, int32_t num_chunks,
+                                   int32_t* local_slices, int32_t max_local, int32_t* num_local,
+                                   int32_t* kv_ranges, int32_t max_kv, int32_t* num_kv);
 
 /* Static description of a status code. */
 FFA_API const char* ffa_status_string(ffa_status status);

@@ -23,7 +23,7 @@ def declared_symbols():
 
 def test_exports_every_declared_symbol():
     names = declared_symbols()
-    assert len(names) == 11 and set(names) == set(ffa.EXPORTED)
+    assert len(names) == 14 and set(names) == set(ffa.EXPORTED)
     L = ffa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -35,8 +35,8 @@ def test_exports_every_declared_symbol():
 
 def test_abi_version_and_strings():
     L = ffa.lib()
-    assert L.ffa_abi_version() == 2
-    for code in range(5):
+    assert L.ffa_abi_version() == 3
+    for code in range(6):
         assert len(L.ffa_status_string(code)) > 0
 
 
