@@ -1,7 +1,6 @@
 // ffa_api.hip - host side of the libffa C ABI: argument validation, metadata
 // layout and kernel dispatch.  Nothing here allocates, synchronises or keeps
 // state; every call only enqueues kernels on the caller's stream.
-#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -78,19 +77,12 @@ BwdWsLayout bwd_ws_layout(const ffa_shape& s) {
 }
 
 // dK/dV workgroups resident at once on the current device (two per compute
-// unit), cached per device.
+// unit); asked on every call, the library keeps no state.
 int resident_dkdv_slots() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
+  int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (dev >= 0 && dev < 64) {
-    const int c = cache[dev].load(std::memory_order_relaxed);
-    if (c > 0) return c;
-  }
-  int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     return 0;
-  if (dev >= 0 && dev < 64) cache[dev].store(2 * cus, std::memory_order_relaxed);
   return 2 * cus;
 }
 
