@@ -29,7 +29,9 @@ EXPORTED = (
     "ffa_block_meta_workspace_size", "ffa_build_block_meta", "ffa_block_meta_view", "ffa_fwd",
     "ffa_bwd_workspace_size", "ffa_bwd", "ffa_bwd_phases", "ffa_status_string", "ffa_abi_version",
     "ffa_fwd_ex", "ffa_bwd_ex", "ffa_chunk_areas", "ffa_dispatch_chunks", "ffa_rank_slices",
+    "ffa_fwd_grouped", "ffa_bwd_grouped",
 )
+MAX_MASK_GROUPS = 8             # FFA_MAX_MASK_GROUPS
 BWD_PRE, BWD_DKDV, BWD_DQ, BWD_ALL = 1, 2, 4, 7
 ACCUMULATE = 1                  # FFA_ACCUMULATE flag of ffa_fwd_ex / ffa_bwd_ex
 
@@ -95,6 +97,13 @@ def lib() -> ctypes.CDLL:
     L.ffa_fwd_ex.restype = st
     L.ffa_bwd_ex.argtypes = L.ffa_bwd.argtypes[:-1] + [i32, ctypes.c_uint32, vp]
     L.ffa_bwd_ex.restype = st
+    L.ffa_fwd_grouped.argtypes = [ctypes.POINTER(Shape), TensorIn, TensorIn, TensorIn, i32, vp, vp,
+                                  TensorOut, vp, ctypes.c_uint32, vp]
+    L.ffa_fwd_grouped.restype = st
+    L.ffa_bwd_grouped.argtypes = [ctypes.POINTER(Shape), TensorIn, TensorIn, TensorIn, TensorIn, vp,
+                                  TensorIn, i32, vp, vp, TensorOut, TensorOut, TensorOut, vp, sz, i32,
+                                  ctypes.c_uint32, vp]
+    L.ffa_bwd_grouped.restype = st
     P32, P64 = ctypes.POINTER(i32), ctypes.POINTER(i64)
     L.ffa_chunk_areas.argtypes = [vp, i32, i32, i32, i32, vp]
     L.ffa_chunk_areas.restype = st
@@ -257,6 +266,56 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, meta: BlockMeta, scal
     return out, lse
 
 
+def _groups(metas, kv_head_end, Hkv):
+    if len(metas) != len(kv_head_end) or not 1 <= len(metas) <= MAX_MASK_GROUPS:
+        raise FFAError("need 1..8 metadata buffers, one per kv-head group")
+    ptrs = (ctypes.c_void_p * len(metas))(*[m.ptr for m in metas])
+    ends = (ctypes.c_int32 * len(metas))(*[int(e) for e in kv_head_end])
+    return len(metas), ptrs, ends
+
+
+def fwd_grouped(q, k, v, metas: Sequence[BlockMeta], kv_head_end: Sequence[int], scale: float = None,
+                out=None, lse=None, stream=None, accumulate: bool = False):
+    """Forward of several masks in one launch: kv heads [kv_head_end[g-1],
+    kv_head_end[g]) and their query heads use metas[g] (ffa_fwd_grouped)."""
+    if accumulate and (out is None or lse is None):
+        raise FFAError("accumulate needs the previous out and lse")
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check_thd(t, n)
+    sh = _shape(q, k, scale)
+    ng, ptrs, ends = _groups(metas, kv_head_end, k.shape[1])
+    out = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
+    if lse is None:
+        lse = torch.empty(q.shape[1], q.shape[0], dtype=torch.float32, device=q.device)
+    _check(lib().ffa_fwd_grouped(ctypes.byref(sh), _tin(q), _tin(k), _tin(v), ng, ptrs, ends,
+                                 _tout(out), lse.data_ptr(), ACCUMULATE if accumulate else 0,
+                                 _stream(stream)), "ffa_fwd_grouped")
+    return out, lse
+
+
+def bwd_grouped(q, k, v, o, lse, do, metas: Sequence[BlockMeta], kv_head_end: Sequence[int],
+                scale: float = None, dq=None, dk=None, dv=None, workspace=None, stream=None,
+                phases: int = BWD_ALL, accumulate: bool = False):
+    """Backward of a grouped forward (ffa_bwd_grouped) -> (dq, dk, dv)."""
+    if accumulate and (dq is None or dk is None or dv is None):
+        raise FFAError("accumulate needs the dq, dk, dv to add to")
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        _check_thd(t, n)
+    sh = _shape(q, k, scale)
+    ng, ptrs, ends = _groups(metas, kv_head_end, k.shape[1])
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+    need = bwd_workspace_size(q, k, scale)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check(lib().ffa_bwd_grouped(ctypes.byref(sh), _tin(q), _tin(k), _tin(v), _tin(o), lse.data_ptr(),
+                                 _tin(do), ng, ptrs, ends, _tout(dq), _tout(dk), _tout(dv),
+                                 workspace.data_ptr(), workspace.numel(), int(phases),
+                                 ACCUMULATE if accumulate else 0, _stream(stream)), "ffa_bwd_grouped")
+    return dq, dk, dv
+
+
 # ------------------------------------------------------------------------
 # Context-parallel dispatch (host only; see ffa.h)
 # ------------------------------------------------------------------------
@@ -360,5 +419,6 @@ def ffa_attention(q, k, v, meta: BlockMeta, scale: float = None) -> torch.Tensor
 
 __all__ = ["BWD_PRE", "BWD_DKDV", "BWD_DQ", "BWD_ALL", "ACCUMULATE", "build_meta", "fwd", "bwd", "ffa_attention", "FFAFunction", "BlockMeta", "lib",
            "meta_workspace_size", "bwd_workspace_size", "chunk_areas", "dispatch_chunks",
+           "fwd_grouped", "bwd_grouped", "MAX_MASK_GROUPS",
            "rank_slices", "FFAError", "FULL", "CAUSAL", "INV_CAUSAL",
            "BI_CAUSAL", "EXPORTED"]

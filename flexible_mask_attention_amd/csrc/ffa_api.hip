@@ -88,6 +88,29 @@ int resident_dkdv_slots() {
 
 }  // namespace
 
+namespace {
+
+// Validate and copy the mask groups of a grouped call.
+ffa_status fill_groups(int32_t n, const void* const* metas, const int32_t* kv_end, int32_t Hkv,
+                       MaskGroups& g) {
+  if (n < 1 || n > FFA_MAX_MASK_GROUPS || !metas || !kv_end) return FFA_ERR_INVALID_ARGUMENT;
+  int32_t prev = 0;
+  for (int32_t j = 0; j < n; ++j) {
+    if (!metas[j] || !aligned(metas[j], 256)) return FFA_ERR_INVALID_ARGUMENT;
+    if (kv_end[j] <= prev) return FFA_ERR_INVALID_ARGUMENT;
+    prev = kv_end[j];
+  }
+  if (prev != Hkv) return FFA_ERR_INVALID_ARGUMENT;
+  for (int32_t j = 0; j < FFA_MAX_MASK_GROUPS; ++j) {
+    g.meta[j] = j < n ? metas[j] : metas[n - 1];
+    g.kv_end[j] = j < n ? kv_end[j] : Hkv;
+  }
+  g.n = n;
+  return FFA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 FFA_API int32_t ffa_abi_version(void) { return FFA_ABI_VERSION; }
@@ -171,6 +194,14 @@ FFA_API ffa_status ffa_fwd(const ffa_shape* shape, ffa_tensor_in q, ffa_tensor_i
 FFA_API ffa_status ffa_fwd_ex(const ffa_shape* shape, ffa_tensor_in q, ffa_tensor_in k,
                               ffa_tensor_in v, const void* d_meta, ffa_tensor_out o, float* lse,
                               uint32_t flags, void* stream) {
+  const int32_t all = shape ? shape->num_heads_kv : 0;
+  return ffa_fwd_grouped(shape, q, k, v, 1, &d_meta, &all, o, lse, flags, stream);
+}
+
+FFA_API ffa_status ffa_fwd_grouped(const ffa_shape* shape, ffa_tensor_in q, ffa_tensor_in k,
+                                   ffa_tensor_in v, int32_t num_groups, const void* const* d_metas,
+                                   const int32_t* kv_head_end, ffa_tensor_out o, float* lse,
+                                   uint32_t flags, void* stream) {
   if (flags & ~FFA_ACCUMULATE) return FFA_ERR_INVALID_ARGUMENT;
   ffa_status st = check_shape(shape);
   if (st != FFA_OK) return st;
@@ -182,16 +213,16 @@ FFA_API ffa_status ffa_fwd_ex(const ffa_shape* shape, ffa_tensor_in q, ffa_tenso
       !check_tensor(v.ptr, v.token_stride, v.head_stride, Tk, Hkv, D))
     return FFA_ERR_INVALID_ARGUMENT;
   if (Tq > 0 && (!lse || !aligned(lse, 16))) return FFA_ERR_INVALID_ARGUMENT;
-  if (!d_meta || !aligned(d_meta, 256)) return FFA_ERR_INVALID_ARGUMENT;
+  FwdArgs a;
+  if (fill_groups(num_groups, d_metas, kv_head_end, Hkv, a.groups) != FFA_OK)
+    return FFA_ERR_INVALID_ARGUMENT;
   if (Tq == 0) return FFA_OK;
   const MetaLayout L = meta_layout(0, Tq, Tk);
-  FwdArgs a;
   a.q = static_cast<const __bf16*>(q.ptr);
   a.k = static_cast<const __bf16*>(k.ptr);
   a.v = static_cast<const __bf16*>(v.ptr);
   a.o = static_cast<__bf16*>(o.ptr);
   a.lse = lse;
-  a.meta = d_meta;
   a.q_ts = q.token_stride;
   a.q_hs = q.head_stride;
   a.k_ts = k.token_stride;
@@ -242,6 +273,17 @@ FFA_API ffa_status ffa_bwd_ex(const ffa_shape* shape, ffa_tensor_in q, ffa_tenso
                               ffa_tensor_in dout, const void* d_meta, ffa_tensor_out dq,
                               ffa_tensor_out dk, ffa_tensor_out dv, void* d_ws, size_t ws_bytes,
                               int32_t phases, uint32_t flags, void* stream) {
+  const int32_t all = shape ? shape->num_heads_kv : 0;
+  return ffa_bwd_grouped(shape, q, k, v, o, lse, dout, 1, &d_meta, &all, dq, dk, dv, d_ws,
+                         ws_bytes, phases, flags, stream);
+}
+
+FFA_API ffa_status ffa_bwd_grouped(const ffa_shape* shape, ffa_tensor_in q, ffa_tensor_in k,
+                                   ffa_tensor_in v, ffa_tensor_in o, const float* lse,
+                                   ffa_tensor_in dout, int32_t num_groups, const void* const* d_metas,
+                                   const int32_t* kv_head_end, ffa_tensor_out dq, ffa_tensor_out dk,
+                                   ffa_tensor_out dv, void* d_ws, size_t ws_bytes, int32_t phases,
+                                   uint32_t flags, void* stream) {
   if (phases & ~FFA_BWD_ALL) return FFA_ERR_INVALID_ARGUMENT;
   if (flags & ~FFA_ACCUMULATE) return FFA_ERR_INVALID_ARGUMENT;
   ffa_status st = check_shape(shape);
@@ -258,14 +300,15 @@ FFA_API ffa_status ffa_bwd_ex(const ffa_shape* shape, ffa_tensor_in q, ffa_tenso
       !check_tensor(dv.ptr, dv.token_stride, dv.head_stride, Tk, Hkv, D))
     return FFA_ERR_INVALID_ARGUMENT;
   if (Tq > 0 && (!lse || !aligned(lse, 16))) return FFA_ERR_INVALID_ARGUMENT;
-  if (!d_meta || !aligned(d_meta, 256)) return FFA_ERR_INVALID_ARGUMENT;
+  BwdArgs a;
+  if (fill_groups(num_groups, d_metas, kv_head_end, Hkv, a.groups) != FFA_OK)
+    return FFA_ERR_INVALID_ARGUMENT;
   size_t need = 0;
   ffa_bwd_workspace_size(shape, &need);
   if (need > 0 && (!d_ws || !aligned(d_ws, 256))) return FFA_ERR_INVALID_ARGUMENT;
   if (ws_bytes < need) return FFA_ERR_WORKSPACE_TOO_SMALL;
   if (Tq == 0 && Tk == 0) return FFA_OK;
   const MetaLayout L = meta_layout(0, Tq, Tk);
-  BwdArgs a;
   a.q = static_cast<const __bf16*>(q.ptr);
   a.k = static_cast<const __bf16*>(k.ptr);
   a.v = static_cast<const __bf16*>(v.ptr);
@@ -287,7 +330,6 @@ FFA_API ffa_status ffa_bwd_ex(const ffa_shape* shape, ffa_tensor_in q, ffa_tenso
   a.dq = static_cast<__bf16*>(dq.ptr);
   a.dk = static_cast<__bf16*>(dk.ptr);
   a.dv = static_cast<__bf16*>(dv.ptr);
-  a.meta = d_meta;
   a.q_ts = q.token_stride;
   a.q_hs = q.head_stride;
   a.k_ts = k.token_stride;

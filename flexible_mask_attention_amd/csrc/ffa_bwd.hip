@@ -93,10 +93,6 @@ __global__ __launch_bounds__(NT, 3) __attribute__((amdgpu_waves_per_eu(3, 3))) v
   constexpr int GB = group_bytes<SK>();
   static_assert(2 * SK == 16 * (NT / 64), "K and V stage tiles are loaded by half of the waves each");
 
-  const MetaView mv = meta_view(a.meta);
-  const FFA_CONST MetaHeader* hd = mv.hdr;
-  if (hd->status != 0 || hd->seqlen_q != a.Tq || hd->seqlen_k != a.Tk) return;
-
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h32 = lane >> 5, t16 = lane & 15, g16 = lane >> 4;
@@ -107,9 +103,12 @@ __global__ __launch_bounds__(NT, 3) __attribute__((amdgpu_waves_per_eu(3, 3))) v
       for (int i = tid; i < a.split_e * a.Hkv; i += NT) a.split_cnt[i] = 0;
   }
   int item, head;
-  xcd_map(blockIdx.x, a.Hq, item, head);
-  const int m = mv.sched_f[item];
+  xcd_map(blockIdx.x, a.Hq, a.Hkv, item, head);
   const int kvh = head / (a.Hq / a.Hkv);
+  const MetaView mv = meta_view(group_meta(a.groups, kvh));
+  const FFA_CONST MetaHeader* hd = mv.hdr;
+  if (hd->status != 0 || hd->seqlen_q != a.Tq || hd->seqlen_k != a.Tk) return;
+  const int m = mv.sched_f[item];
   const int qrow = m * BM_F + wid * 32 + l32;
   const bool qok = qrow < a.Tq;
 

@@ -36,20 +36,20 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   constexpr int MB = D / 32;
   constexpr int KS = D / 16;
 
-  const MetaView mv = meta_view(a.meta);
-  const FFA_CONST MetaHeader* hd = mv.hdr;
-  if (hd->status != 0 || hd->seqlen_q != a.Tq || hd->seqlen_k != a.Tk) return;
-
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h32 = lane >> 5, t16 = lane & 15, g16 = lane >> 4;
   int item, kvh;
-  xcd_map(blockIdx.x, a.Hkv, item, kvh);
+  xcd_map(blockIdx.x, a.Hkv, a.Hkv, item, kvh);
+  const MetaView mv = meta_view(group_meta(a.groups, kvh));
+  const FFA_CONST MetaHeader* hd = mv.hdr;
+  if (hd->status != 0 || hd->seqlen_q != a.Tq || hd->seqlen_k != a.Tk) return;
   // Items [0, 2 split_e) are the two halves of the split_e longest blocks (the
   // schedule is longest first); a candidate is split only if its work exceeds
   // what one resident workgroup would get with the whole backward spread
-  // evenly, cost * slots > Hkv * total cost (the query heads per kv head
-  // cancel), otherwise its first item does all of it and the second exits.
+  // evenly, cost * slots > sum over kv heads of their total cost (the query
+  // heads per kv head cancel), otherwise its first item does all of it and
+  // the second exits.
   int part = -1, cand = 0, n;
   if (item < 2 * a.split_e) {
     cand = item >> 1;
@@ -66,8 +66,15 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   const int nT = nP + nF;
   if (item < 2 * a.split_e) {
     const int64_t cost = 4LL * nF + 5LL * nP;
-    const int64_t tot = 4LL * hd->nnz[L_KF] + 5LL * hd->nnz[L_KM];
-    if (cost * a.split_slots > tot * a.Hkv && G * nT >= 4) part = item & 1;
+    int64_t work = 0;
+#pragma unroll
+    for (int j = 0; j < FFA_MAX_MASK_GROUPS; ++j)
+      if (j < a.groups.n) {
+        const FFA_CONST MetaHeader* hj = (const FFA_CONST MetaHeader*)a.groups.meta[j];
+        const int heads = a.groups.kv_end[j] - (j ? a.groups.kv_end[j - 1] : 0);
+        work += heads * (4LL * hj->nnz[L_KF] + 5LL * hj->nnz[L_KM]);
+      }
+    if (cost * a.split_slots > work && G * nT >= 4) part = item & 1;
     else if (item & 1) return;
   }
   cint32_t* fidx = mv.var + hd->list_off[L_KF] + f0;

@@ -46,17 +46,16 @@ void ffa_fwd_kernel(FwdArgs a) {
   constexpr int GB = group_bytes<SK>();
   constexpr int HALVES = BN_F / SK;
 
-  const MetaView mv = meta_view(a.meta);
-  const FFA_CONST MetaHeader* hd = mv.hdr;
-  if (hd->status != 0 || hd->seqlen_q != a.Tq || hd->seqlen_k != a.Tk) return;
-
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int l32 = lane & 31, h32 = lane >> 5, t16 = lane & 15, g16 = lane >> 4;
   int item, head;
-  xcd_map(blockIdx.x, a.Hq, item, head);
-  const int m = mv.sched_f[item];
+  xcd_map(blockIdx.x, a.Hq, a.Hkv, item, head);
   const int kvh = head / (a.Hq / a.Hkv);
+  const MetaView mv = meta_view(group_meta(a.groups, kvh));
+  const FFA_CONST MetaHeader* hd = mv.hdr;
+  if (hd->status != 0 || hd->seqlen_q != a.Tq || hd->seqlen_k != a.Tk) return;
+  const int m = mv.sched_f[item];
   const int row0 = m * BM_F + wid * RW + l32;   // this lane's query row
 
   const int f0 = mv.qf_off[m], nF = mv.qf_off[m + 1] - f0;

@@ -294,21 +294,24 @@ struct TileDma {
   }
 };
 
-// Work items are (schedule position, head) pairs, nitems * H blocks in all.
-// Blocks are dispatched round-robin over the 8 XCDs (block b on XCD b % 8),
-// each with its own L2.  When H is a multiple of 8, XCD x is given the heads
-// [x H/8, (x+1) H/8) and takes their items in schedule order (heaviest
+// Work items are (schedule position, head) pairs, nitems * Hq blocks in all
+// (Hq = Hkv for the key-major kernel).  Blocks are dispatched round-robin
+// over the 8 XCDs (block b on XCD b % 8), each with its own L2.  When Hkv is a
+// multiple of 8, XCD x is given the kv heads x, x + 8, x + 16, ... with all
+// their query heads and takes their items in schedule order (heaviest
 // first), head-minor: consecutive blocks on one XCD are the heads of one
-// item, which share key/value (or query) tiles through that XCD's L2, and
-// every XCD receives the same amount of work.
-__device__ __forceinline__ void xcd_map(int bid, int H, int& item, int& head) {
-  if (H % 8 == 0) {
-    const int hx = H / 8, x = bid & 7, j = bid >> 3;
+// item, which share key/value (or query) tiles through that XCD's L2; taking
+// every eighth kv head (not a contiguous range) spreads kv-head groups with
+// different masks over all XCDs.
+__device__ __forceinline__ void xcd_map(int bid, int Hq, int Hkv, int& item, int& head) {
+  if (Hkv % 8 == 0) {
+    const int G = Hq / Hkv, hx = (Hkv / 8) * G, x = bid & 7, j = bid >> 3;
+    const int r = j % hx;
     item = j / hx;
-    head = x * hx + j % hx;
+    head = (x + 8 * (r / G)) * G + r % G;
   } else {
-    item = bid / H;
-    head = bid % H;
+    item = bid / Hq;
+    head = bid % Hq;
   }
 }
 
@@ -330,13 +333,30 @@ hipError_t launch_build_meta(const int32_t* d_slices, int32_t S, int32_t Tq, int
                              int32_t head_dim, void* d_meta, int64_t capacity,
                              const MetaLayout& L, hipStream_t stream);
 
+// Metadata per kv-head group: kv heads [kv_end[g-1], kv_end[g]) use meta[g].
+struct MaskGroups {
+  const void* meta[FFA_MAX_MASK_GROUPS];
+  int32_t kv_end[FFA_MAX_MASK_GROUPS];
+  int32_t n;
+};
+
+// The metadata of kv head kvh (a chain of selects: no indexing into the
+// kernel-argument array).
+__device__ __forceinline__ const void* group_meta(const MaskGroups& g, int kvh) {
+  const void* m = g.meta[0];
+#pragma unroll
+  for (int j = 1; j < FFA_MAX_MASK_GROUPS; ++j)
+    if (j < g.n && kvh >= g.kv_end[j - 1]) m = g.meta[j];
+  return m;
+}
+
 struct FwdArgs {
   const __bf16* q;
   const __bf16* k;
   const __bf16* v;
   __bf16* o;
   float* lse;
-  const void* meta;
+  MaskGroups groups;
   int64_t q_ts, q_hs, k_ts, k_hs, v_ts, v_hs, o_ts, o_hs;
   int32_t Tq, Tk, Hq, Hkv;
   float scale_log2;   // softmax_scale * log2(e)
@@ -357,7 +377,7 @@ struct BwdArgs {
   __bf16* dq;
   __bf16* dk;
   __bf16* dv;
-  const void* meta;
+  MaskGroups groups;
   int64_t q_ts, q_hs, k_ts, k_hs, v_ts, v_hs, o_ts, o_hs, do_ts, do_hs;
   int64_t dq_ts, dq_hs, dk_ts, dk_hs, dv_ts, dv_hs;
   int32_t Tq, Tk, Hq, Hkv;

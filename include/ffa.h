@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define FFA_ABI_VERSION 3
+#define FFA_ABI_VERSION 4
 
 #if defined(__GNUC__)
 #define FFA_API __attribute__((visibility("default")))
@@ -239,6 +239,39 @@ FFA_API ffa_status ffa_bwd_ex(const ffa_shape* shape, ffa_tensor_in q, ffa_tenso
                               ffa_tensor_in dout, const void* d_meta, ffa_tensor_out dq,
                               ffa_tensor_out dk, ffa_tensor_out dv, void* d_ws, size_t ws_bytes,
                               int32_t phases, uint32_t flags, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Several masks in one launch.
+ *
+ * The kv heads are cut into num_groups consecutive ranges, group g being kv
+ * heads [kv_head_end[g-1], kv_head_end[g]) (kv_head_end[-1] = 0), together with
+ * the query heads that read them; each group has its own slice table, i.e. its
+ * own metadata buffer d_metas[g], all built for the shape's seqlen_q, seqlen_k
+ * and head_dim.  One launch covers every group, so a model whose head groups
+ * use different masks (or a layer that reuses the metadata of several masks)
+ * needs one call instead of one per mask, and no group waits for another's
+ * tail (MagiAttention docs, magi_attn_flex_key / make_flex_key_for_new_mask_after_dispatch:
+ * metadata built once per mask and reused).  Results per head are those of a
+ * single-mask call with that group's metadata, except that the dK/dV load
+ * balancing (see ffa_bwd) weighs every group's work.
+ * num_groups in 1..FFA_MAX_MASK_GROUPS; kv_head_end: host int32 [num_groups],
+ * strictly increasing, last = num_heads_kv; d_metas: host array of
+ * num_groups device pointers (256-byte aligned).  Bad groups give
+ * FFA_ERR_INVALID_ARGUMENT.
+ * ------------------------------------------------------------------------- */
+#define FFA_MAX_MASK_GROUPS 8
+
+FFA_API ffa_status ffa_fwd_grouped(const ffa_shape* shape, ffa_tensor_in q, ffa_tensor_in k,
+                                   ffa_tensor_in v, int32_t num_groups, const void* const* d_metas,
+                                   const int32_t* kv_head_end, ffa_tensor_out o, float* lse,
+                                   uint32_t flags, void* stream);
+
+FFA_API ffa_status ffa_bwd_grouped(const ffa_shape* shape, ffa_tensor_in q, ffa_tensor_in k,
+                                   ffa_tensor_in v, ffa_tensor_in o, const float* lse,
+                                   ffa_tensor_in dout, int32_t num_groups, const void* const* d_metas,
+                                   const int32_t* kv_head_end, ffa_tensor_out dq, ffa_tensor_out dk,
+                                   ffa_tensor_out dv, void* d_ws, size_t ws_bytes, int32_t phases,
+                                   uint32_t flags, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Context-parallel dispatch (host only: no device memory, no stream).

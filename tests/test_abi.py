@@ -23,7 +23,7 @@ def declared_symbols():
 
 def test_exports_every_declared_symbol():
     names = declared_symbols()
-    assert len(names) == 14 and set(names) == set(ffa.EXPORTED)
+    assert len(names) == 16 and set(names) == set(ffa.EXPORTED)
     L = ffa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol():
 
 def test_abi_version_and_strings():
     L = ffa.lib()
-    assert L.ffa_abi_version() == 3
+    assert L.ffa_abi_version() == 4
     for code in range(6):
         assert len(L.ffa_status_string(code)) > 0
 
@@ -89,6 +89,28 @@ def test_host_validation_returns_before_enqueue():
                         0x100000, ws.value, 7, 4, None) == 1
     assert L.ffa_bwd_ex(P(_shape()), good, good, good, good, lse, good, meta, goodo, goodo, goodo,
                         0x100000, ws.value - 1, 7, 1, None) == 3
+    # grouped calls: group count, order, coverage of the kv heads, alignment
+    Metas = ctypes.c_void_p * 3
+    Ends = ctypes.c_int32 * 3
+    sh = _shape(Hq=4, Hkv=2)
+    ok_m, ok_e = Metas(0x10000, 0x20000, 0), Ends(1, 2, 0)
+    assert L.ffa_fwd_grouped(P(sh), good, good, good, 0, ok_m, ok_e, goodo, lse, 0, None) == 1
+    assert L.ffa_fwd_grouped(P(sh), good, good, good, 9, ok_m, ok_e, goodo, lse, 0, None) == 1
+    assert L.ffa_fwd_grouped(P(sh), good, good, good, 2, Metas(0x10000, 0x20010, 0), ok_e, goodo, lse, 0, None) == 1
+    assert L.ffa_fwd_grouped(P(sh), good, good, good, 2, ok_m, Ends(2, 1, 0), goodo, lse, 0, None) == 1
+    assert L.ffa_fwd_grouped(P(sh), good, good, good, 2, ok_m, Ends(1, 3, 0), goodo, lse, 0, None) == 1
+    assert L.ffa_fwd_grouped(P(sh), good, good, good, 1, ok_m, Ends(1, 0, 0), goodo, lse, 0, None) == 1
+    assert L.ffa_fwd_grouped(P(sh), good, good, good, 2, None, ok_e, goodo, lse, 0, None) == 1
+    # the same checks pass for good groups (an empty query range then enqueues nothing)
+    sh0 = _shape(Tq=0, Hq=4, Hkv=2)
+    assert L.ffa_fwd_grouped(P(sh0), good, good, good, 2, ok_m, ok_e, goodo, lse, 0, None) == 0
+    assert L.ffa_fwd_grouped(P(sh0), good, good, good, 2, ok_m, Ends(2, 2, 0), goodo, lse, 0, None) == 1
+    wsg = ctypes.c_size_t()
+    assert L.ffa_bwd_workspace_size(P(sh), P(wsg)) == 0
+    assert L.ffa_bwd_grouped(P(sh), good, good, good, good, lse, good, 2, ok_m, Ends(1, 1, 0), goodo,
+                             goodo, goodo, 0x100000, wsg.value, 7, 0, None) == 1
+    assert L.ffa_bwd_grouped(P(sh), good, good, good, good, lse, good, 2, ok_m, ok_e, goodo,
+                             goodo, goodo, 0x100000, wsg.value - 1, 7, 0, None) == 3
     # metadata build: bad sizes, misaligned buffer, too-small buffer
     n = ctypes.c_size_t()
     assert L.ffa_block_meta_workspace_size(-1, 10, 10, 64, None, P(n)) == 1
