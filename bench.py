@@ -76,6 +76,47 @@ class Case:
         self.bwd()
 
 
+class GroupedCase:
+    """All calls of a workload (same sequence lengths and head_dim) as one
+    grouped launch: one tensor set with the calls' heads side by side, each
+    call's kv heads with its own metadata (ffa_fwd_grouped / ffa_bwd_grouped)."""
+
+    def __init__(self, calls, seed, dev):
+        self.parts = [Case(c, seed + i, dev) for i, c in enumerate(calls)]
+        c0 = calls[0]
+        assert all((c.Tq, c.Tk, c.d) == (c0.Tq, c0.Tk, c0.d) for c in calls)
+        for n in ("q", "k", "v", "do"):
+            setattr(self, n, torch.cat([getattr(p, n) for p in self.parts], dim=1).contiguous())
+        for p in self.parts:      # keep only the metadata of the parts
+            for n in ("q", "k", "v", "do", "o", "lse", "dq", "dk", "dv", "ws"):
+                setattr(p, n, None)
+        self.metas = [p.meta for p in self.parts]
+        self.kv_end, e = [], 0
+        for c in calls:
+            e += c.Hkv
+            self.kv_end.append(e)
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty(self.q.shape[1], c0.Tq, dtype=torch.float32, device=dev)
+        self.dq, self.dk, self.dv = torch.empty_like(self.q), torch.empty_like(self.k), torch.empty_like(self.v)
+        self.ws = torch.empty(max(256, ffa.bwd_workspace_size(self.q, self.k)), dtype=torch.uint8, device=dev)
+
+    def build_meta(self):
+        for p in self.parts:
+            p.build_meta()
+
+    def fwd(self):
+        ffa.fwd_grouped(self.q, self.k, self.v, self.metas, self.kv_end, out=self.o, lse=self.lse)
+
+    def bwd(self, phases=ffa.BWD_ALL):
+        ffa.bwd_grouped(self.q, self.k, self.v, self.o, self.lse, self.do, self.metas, self.kv_end,
+                        dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws, phases=phases)
+
+    def step(self):
+        self.build_meta()
+        self.fwd()
+        self.bwd()
+
+
 def phase_times(cases, reps):
     """Average device time (ms) of each phase, from HIP events on the stream the
     library launches on (torch's current stream)."""
@@ -197,6 +238,9 @@ def main():
                     help="meta|fwd|bwd_dkdv|bwd_dq|copy: only launch that phase --reps times "
                          "(for hardware-counter runs); prints no JSON")
     ap.add_argument("--reps", type=int, default=3)
+    ap.add_argument("--grouped", action="store_true",
+                    help="run a workload of several calls (the 128K video workload's two head "
+                         "groups) as one grouped launch over one tensor set")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         log("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -205,15 +249,23 @@ def main():
 
     dev = torch.device("cuda:0")
     W = wl.workload(args.workload)
-    cases = [Case(c, 100 * W.seed + i, dev) for i, c in enumerate(W.calls)]
+    if args.grouped:
+        if len(W.calls) < 2:
+            log("--grouped needs a workload of several calls (workload 4)")
+            sys.exit(2)
+        cases = [GroupedCase(W.calls, 100 * W.seed, dev)]
+        parts = cases[0].parts
+    else:
+        cases = [Case(c, 100 * W.seed + i, dev) for i, c in enumerate(W.calls)]
+        parts = cases
     torch.cuda.synchronize()
-    areas = [cs.meta.area() for cs in cases]
-    for cs in cases:
-        assert cs.meta.status() == 0
+    areas = [p.meta.area() for p in parts]
+    for p in parts:
+        assert p.meta.status() == 0
     if args.profile_phase:
         profile_phase(cases, args.profile_phase, args.reps)
         return
-    f_fwd = sum(4.0 * cs.c.d * a * cs.c.Hq for cs, a in zip(cases, areas))
+    f_fwd = sum(4.0 * p.c.d * a * p.c.Hq for p, a in zip(parts, areas))
     f_bwd = 2.5 * f_fwd
 
     for _ in range(args.warmup):
@@ -256,7 +308,9 @@ def main():
                    "num_heads_q": sum(c.Hq for c in W.calls), "num_heads_kv": sum(c.Hkv for c in W.calls),
                    "head_dim": c0.d, "num_slices": sum(len(c.slices) for c in W.calls),
                    "mask_area": sum(areas), "flops_fwd": f_fwd, "flops_bwd": f_bwd, "seed": W.seed,
-                   "step": "block metadata + forward + backward"},
+                   "step": "block metadata + forward + backward",
+                   "launch": "grouped (one launch for all head groups)" if args.grouped
+                   else "one call per slice table"},
         "fwd_tflops": round(f_fwd / t_fwd / 1e12, 1),
         "fwd_pct_peak": round(100 * f_fwd / t_fwd / 1e12 / PEAK_BF16_TFLOPS, 2),
         "bwd_tflops": round(f_bwd / t_bwd / 1e12, 1),

@@ -235,6 +235,7 @@ FFA_API ffa_status ffa_fwd_grouped(const ffa_shape* shape, ffa_tensor_in q, ffa_
   a.Tk = Tk;
   a.Hq = Hq;
   a.Hkv = Hkv;
+  a.nitems = L.nq_f;
   a.scale = shape->softmax_scale;
   a.scale_log2 = shape->softmax_scale * LOG2E;
   a.flags = flags;
@@ -350,6 +351,8 @@ FFA_API ffa_status ffa_bwd_grouped(const ffa_shape* shape, ffa_tensor_in q, ffa_
   a.Tk = Tk;
   a.Hq = Hq;
   a.Hkv = Hkv;
+  a.nq_f = L.nq_f;
+  a.nk_b = L.nk_b;
   a.scale = shape->softmax_scale;
   a.scale_log2 = shape->softmax_scale * LOG2E;
   a.flags = flags;

@@ -103,7 +103,7 @@ __global__ __launch_bounds__(NT, 3) __attribute__((amdgpu_waves_per_eu(3, 3))) v
       for (int i = tid; i < a.split_e * a.Hkv; i += NT) a.split_cnt[i] = 0;
   }
   int item, head;
-  xcd_map(blockIdx.x, a.Hq, a.Hkv, item, head);
+  xcd_map(blockIdx.x, a.nq_f, a.Hq, a.Hkv, item, head);
   const int kvh = head / (a.Hq / a.Hkv);
   const MetaView mv = meta_view(group_meta(a.groups, kvh));
   const FFA_CONST MetaHeader* hd = mv.hdr;

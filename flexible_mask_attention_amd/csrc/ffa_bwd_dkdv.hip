@@ -40,7 +40,7 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h32 = lane >> 5, t16 = lane & 15, g16 = lane >> 4;
   int item, kvh;
-  xcd_map(blockIdx.x, a.Hkv, a.Hkv, item, kvh);
+  xcd_map(blockIdx.x, a.nk_b + a.split_e, a.Hkv, a.Hkv, item, kvh);
   const MetaView mv = meta_view(group_meta(a.groups, kvh));
   const FFA_CONST MetaHeader* hd = mv.hdr;
   if (hd->status != 0 || hd->seqlen_q != a.Tq || hd->seqlen_k != a.Tk) return;

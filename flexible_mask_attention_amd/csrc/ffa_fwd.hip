@@ -50,7 +50,7 @@ void ffa_fwd_kernel(FwdArgs a) {
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int l32 = lane & 31, h32 = lane >> 5, t16 = lane & 15, g16 = lane >> 4;
   int item, head;
-  xcd_map(blockIdx.x, a.Hq, a.Hkv, item, head);
+  xcd_map(blockIdx.x, a.nitems, a.Hq, a.Hkv, item, head);
   const int kvh = head / (a.Hq / a.Hkv);
   const MetaView mv = meta_view(group_meta(a.groups, kvh));
   const FFA_CONST MetaHeader* hd = mv.hdr;

@@ -297,18 +297,19 @@ struct TileDma {
 // Work items are (schedule position, head) pairs, nitems * Hq blocks in all
 // (Hq = Hkv for the key-major kernel).  Blocks are dispatched round-robin
 // over the 8 XCDs (block b on XCD b % 8), each with its own L2.  When Hkv is a
-// multiple of 8, XCD x is given the kv heads x, x + 8, x + 16, ... with all
-// their query heads and takes their items in schedule order (heaviest
-// first), head-minor: consecutive blocks on one XCD are the heads of one
-// item, which share key/value (or query) tiles through that XCD's L2; taking
+// multiple of 8, XCD x is given the kv heads x, x + 8, x + 16, ... and works
+// through them one after the other; for each it takes the items in schedule
+// order (heaviest first), head-minor: consecutive blocks on one XCD are the
+// query heads of one item, which share key/value (or query) tiles through
+// that XCD's L2, and one kv head's working set at a time stays in it.  Taking
 // every eighth kv head (not a contiguous range) spreads kv-head groups with
 // different masks over all XCDs.
-__device__ __forceinline__ void xcd_map(int bid, int Hq, int Hkv, int& item, int& head) {
+__device__ __forceinline__ void xcd_map(int bid, int nitems, int Hq, int Hkv, int& item, int& head) {
   if (Hkv % 8 == 0) {
-    const int G = Hq / Hkv, hx = (Hkv / 8) * G, x = bid & 7, j = bid >> 3;
-    const int r = j % hx;
-    item = j / hx;
-    head = (x + 8 * (r / G)) * G + r % G;
+    const int G = Hq / Hkv, per_kv = nitems * G, x = bid & 7, j = bid >> 3;
+    const int r = j % per_kv;
+    item = r / G;
+    head = (x + 8 * (j / per_kv)) * G + r % G;
   } else {
     item = bid / Hq;
     head = bid % Hq;
@@ -359,6 +360,7 @@ struct FwdArgs {
   MaskGroups groups;
   int64_t q_ts, q_hs, k_ts, k_hs, v_ts, v_hs, o_ts, o_hs;
   int32_t Tq, Tk, Hq, Hkv;
+  int32_t nitems;     // query blocks (the grid is nitems * Hq)
   float scale_log2;   // softmax_scale * log2(e)
   float scale;
   uint32_t flags;     // FFA_ACCUMULATE: merge into the (o, lse) already in the buffers
@@ -381,6 +383,7 @@ struct BwdArgs {
   int64_t q_ts, q_hs, k_ts, k_hs, v_ts, v_hs, o_ts, o_hs, do_ts, do_hs;
   int64_t dq_ts, dq_hs, dk_ts, dk_hs, dv_ts, dv_hs;
   int32_t Tq, Tk, Hq, Hkv;
+  int32_t nq_f, nk_b; // query blocks of the dQ grid, key blocks of the dK/dV grid
   float scale_log2;
   float scale;
   uint32_t flags;     // FFA_ACCUMULATE: add to the dq / dk / dv already in the buffers
