@@ -398,23 +398,33 @@ def bwd(q, k, v, o, lse, do, meta: BlockMeta, scale: float = None, dq=None, dk=N
 
 
 class FFAFunction(torch.autograd.Function):
+    """Autograd wrapper: ``meta`` is one BlockMeta, or a list of them with
+    ``kv_head_end`` for several masks in one launch."""
+
     @staticmethod
-    def forward(ctx, q, k, v, meta, scale):
-        o, lse = fwd(q, k, v, meta, scale)
+    def forward(ctx, q, k, v, meta, scale, kv_head_end=None):
+        if isinstance(meta, (list, tuple)):
+            o, lse = fwd_grouped(q, k, v, meta, kv_head_end, scale)
+        else:
+            o, lse = fwd(q, k, v, meta, scale)
         ctx.save_for_backward(q, k, v, o, lse)
-        ctx.meta, ctx.scale = meta, scale
+        ctx.meta, ctx.scale, ctx.kv_head_end = meta, scale, kv_head_end
         return o
 
     @staticmethod
     def backward(ctx, do):
         q, k, v, o, lse = ctx.saved_tensors
-        dq, dk, dv = bwd(q, k, v, o, lse, do.contiguous(), ctx.meta, ctx.scale)
-        return dq, dk, dv, None, None
+        do = do.contiguous()
+        if isinstance(ctx.meta, (list, tuple)):
+            dq, dk, dv = bwd_grouped(q, k, v, o, lse, do, ctx.meta, ctx.kv_head_end, ctx.scale)
+        else:
+            dq, dk, dv = bwd(q, k, v, o, lse, do, ctx.meta, ctx.scale)
+        return dq, dk, dv, None, None, None
 
 
-def ffa_attention(q, k, v, meta: BlockMeta, scale: float = None) -> torch.Tensor:
-    """Flex-Flash-Attention with autograd support."""
-    return FFAFunction.apply(q, k, v, meta, scale)
+def ffa_attention(q, k, v, meta, scale: float = None, kv_head_end=None) -> torch.Tensor:
+    """Flex-Flash-Attention with autograd support (see FFAFunction)."""
+    return FFAFunction.apply(q, k, v, meta, scale, kv_head_end)
 
 
 __all__ = ["BWD_PRE", "BWD_DKDV", "BWD_DQ", "BWD_ALL", "ACCUMULATE", "build_meta", "fwd", "bwd", "ffa_attention", "FFAFunction", "BlockMeta", "lib",
