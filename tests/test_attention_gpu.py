@@ -2,7 +2,7 @@
 
 Tolerances (bf16 inputs, fp32 accumulation): O elementwise |d| <= 1e-2 + 1e-2|ref|;
 LSE |d| <= 1e-3 with -inf matching -inf; dQ, dK, dV relative Frobenius error
-<= 2e-2 over the checked rows.
+<= 2e-2 over the checked rows (a zero reference: norm <= 2^-16 sqrt(n)).
 
 * small and medium cases (several tiles, ragged tails, every mask type, GQA,
   both head dims): every output element against the oracle;
@@ -58,7 +58,10 @@ def check_grad(got, ref, what):
     nr = np.linalg.norm(ref)
     ne = np.linalg.norm(g - ref)
     if nr == 0:
-        assert ne == 0, f"{what}: expected zero, got norm {ne:.3g}"
+        # a zero reference, e.g. a row whose single key makes dS = P (dP - D)
+        # vanish: the kernel forms P and D in fp32 from the bf16 O and the fp32
+        # LSE, so it returns rounding noise; bound it at fp32 level
+        assert ne <= 2.0 ** -16 * math.sqrt(g.size), f"{what}: expected zero, got norm {ne:.3g}"
         return
     rel = ne / nr
     assert rel <= 2e-2, f"{what}: relative Frobenius error {rel:.3g}"
@@ -112,6 +115,25 @@ def test_random_tables(d, seed):
     c = wl.Call(sl, Tq, Tk, Hq, Hkv, d)
     _say(f"random table seed={seed} d={d}: Tq={Tq} Tk={Tk} Hq={Hq} Hkv={Hkv} slices={sl}")
     full_check(c, wl.make_tensors(c, 1000 + seed))
+
+
+@pytest.mark.parametrize("Tq,Tk,Hq,Hkv,d", [
+    (1, 1, 1, 1, 64), (1, 300, 2, 1, 128), (300, 1, 2, 2, 64), (129, 65, 8, 1, 128),
+    (64, 64, 16, 2, 64), (257, 511, 3, 3, 128)])
+def test_boundary_shapes(Tq, Tk, Hq, Hkv, d):
+    """Single-token query or key ranges, one head, GQA with 8 query heads per
+    kv head, sizes one past a tile boundary: every mask type where it fits."""
+    rng = random.Random(Tq * 1000 + Tk)
+    sl = []
+    if Tq >= 2 and Tk >= 2:
+        a, b = Tq // 2, Tk // 2
+        sl = [(0, a, 0, b, ffa.CAUSAL), (a, Tq, b, Tk, ffa.INV_CAUSAL),
+              (0, a, b, Tk, ffa.BI_CAUSAL), (a, Tq, 0, b, ffa.FULL)]
+    else:
+        sl = [(0, Tq, 0, Tk, rng.choice([ffa.FULL, ffa.CAUSAL]))]
+    c = wl.Call(sl, Tq, Tk, Hq, Hkv, d)
+    _say(f"boundary Tq={Tq} Tk={Tk} Hq={Hq} Hkv={Hkv} d={d}: {sl}")
+    full_check(c, wl.make_tensors(c, Tq + 7 * Tk))
 
 
 def test_backward_phases_separately_match_one_call():
