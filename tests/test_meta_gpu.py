@@ -114,3 +114,28 @@ def test_meta_status_flags():
     m = ffa.build_meta(sl, 16384, 16384, 128, out=guard[:fixed + 256])
     assert m.status() & ffa.META_ERR_CAPACITY
     assert bool((guard[fixed + 256:] == 0x5A).all())
+
+
+def test_meta_and_attention_with_thousands_of_slices():
+    """3,000 short causal sequences plus FULL cross-sequence blocks (long
+    per-block slice lists, many slices per tile): metadata bit-exact, and the
+    attention on it against the oracle."""
+    rng = random.Random(99)
+    lens = [rng.randint(1, 16) for _ in range(3000)]
+    sl, s = [], 0
+    for L in lens:
+        sl.append((s, s + L, s, s + L, wl.CAUSAL))
+        s += L
+    T = s
+    # every 50th sequence also sees the 8 tokens before its start (a FULL
+    # slice over keys left of its own range: disjoint from the causal ones)
+    s = 0
+    for i, L in enumerate(lens):
+        if i % 50 == 0 and s >= 8:
+            sl.append((s, s + L, s - 8, s, wl.FULL))
+        s += L
+    _say(f"{len(sl)} slices over {T} tokens")
+    check_meta(sl, T, T, 64)
+    from tests.test_attention_gpu import full_check
+    c = wl.Call(sl, T, T, 2, 1, 64)
+    full_check(c, wl.make_tensors(c, 5))
