@@ -181,7 +181,9 @@ FFA_API ffa_status ffa_bwd_workspace_size(const ffa_shape* shape, size_t* bytes)
  * device's resident workgroups is done as two halves of that order whose fp32
  * sums are added once (a commutative step), so results are bitwise
  * reproducible on a given device; the split choice depends on the number of
- * compute units.  Calls that share one workspace must not run concurrently.
+ * compute units.  Calls that share one workspace must not run concurrently,
+ * except the DQ-only and DKDV-only calls of ffa_bwd_phases after PRE (they
+ * only read the row statistics, and only DKDV uses the split counters).
  * d_ws: device scratch of at least ffa_bwd_workspace_size bytes, 256-byte aligned. */
 FFA_API ffa_status ffa_bwd(const ffa_shape* shape, ffa_tensor_in q, ffa_tensor_in k,
                            ffa_tensor_in v, ffa_tensor_in o, const float* lse,
