@@ -5,7 +5,8 @@
 // level parallelism with atomic reduction of partials).  This backward is the
 // textbook gradient of masked softmax attention written so that every output
 // element has one owner and a fixed summation order, hence bitwise
-// reproducible results without atomics:
+// reproducible results without atomic accumulation (the two halves of a split
+// dK/dV block meet through a counter and add their fp32 partials once):
 //
 //   bwd_pre : -D_i = -dO_i . O_i, LSE_i log2 e          (fp32, [Hq][Tq])
 //   dkdv    : owner (kv head, 128-key block), in ffa_bwd_dkdv.hip

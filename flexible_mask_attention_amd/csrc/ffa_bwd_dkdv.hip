@@ -1,11 +1,11 @@
 // ffa_bwd_dkdv.hip - dK and dV of Flex-Flash-Attention on gfx950.
 //
-// Owner (kv head, 128-key block); loops over the query heads that share the kv
-// head and the k2q tiles of the block, in a fixed order, so dK and dV are
-// bitwise reproducible (the few longest blocks are done as two halves whose
-// fp32 sums are added once, see below) (the backward of the MagiAttention
-// pages' FFA kernel, blog deep-dive, section "Flex-Flash-Attention 与
-// AttnSlice", Fig. 5, written with one owner per output):
+// The backward of the MagiAttention pages' FFA kernel (blog deep-dive, section
+// "Flex-Flash-Attention 与 AttnSlice", Fig. 5), written with one owner per
+// output: owner (kv head, 128-key block), which loops over the query heads
+// that share the kv head and the k2q tiles of the block in a fixed order, so
+// dK and dV are bitwise reproducible; the few longest blocks are done as two
+// halves whose fp32 sums are added once (the split epilogue below):
 //   S = Q K^T, P = exp(S - LSE) (masked on Partial tiles), dV += P^T dO,
 //   dP = dO V^T, dS = P (dP - D), dK += dS^T Q.
 // Each lane owns one key (S = Q K^T leaves keys on lanes), so P and dS feed the
