@@ -142,15 +142,23 @@ def phase_times(cases, reps):
     return {n: tot[n] / reps for n in names}
 
 
-def kernel_source_digest():
-    """sha256 over the HIP sources; recorded hardware counters are only used
-    while the kernels they were taken on are unchanged."""
+def source_code_digest(csrc):
+    """sha256 over the code of the HIP sources in directory ``csrc``: ``//``
+    comments, trailing blanks and empty lines are dropped, so only a change
+    of the code itself changes it (the sources use no other comment form)."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "flexible_mask_attention_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + b"\0" + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            lines = [ln.split("//", 1)[0].rstrip() for ln in fh]
+        code = "\n".join(ln for ln in lines if ln)
+        h.update(f.encode() + b"\0" + code.encode())
     return h.hexdigest()
+
+
+def kernel_source_digest():
+    """Digest of the library's HIP code; recorded hardware counters are only
+    used while the kernels they were taken on are unchanged."""
+    return source_code_digest(os.path.join(ROOT, "flexible_mask_attention_amd", "csrc"))
 
 
 def recorded_traffic(kernel, workload):

@@ -137,3 +137,17 @@ def test_meta_workspace_bound_covers_actual_lists(idx):
         nq = -(-c.Tq // 128)
         nslices_lists = sum((s[1] - 1) // 128 - s[0] // 128 + 1 for s in c.slices if s[1] > s[0])
         assert nbytes >= 4 * (entries + nslices_lists)
+
+
+def test_source_digest_ignores_comments_only(tmp_path):
+    """The digest that keys recorded hardware counters changes with the code
+    of the HIP sources, not with their comments."""
+    import bench
+    d = tmp_path / "csrc"
+    d.mkdir()
+    (d / "a.hip").write_text("int f() {  // one\n  return 1;\n}\n")
+    base = bench.source_code_digest(str(d))
+    (d / "a.hip").write_text("// header\nint f() {  // two\n\n  return 1;   \n}\n")
+    assert bench.source_code_digest(str(d)) == base
+    (d / "a.hip").write_text("int f() {\n  return 2;\n}\n")
+    assert bench.source_code_digest(str(d)) != base
