@@ -108,3 +108,60 @@ def test_video_workload_as_one_grouped_call():
         for a, b in ((g1[1], dk[:, h]), (g1[2], dv[:, h])):
             rel = float((a.double() - b.double()).norm() / max(float(a.double().norm()), 1e-30))
             assert rel <= 1e-2
+
+
+def test_grouped_with_accumulate_over_split_tables():
+    """Each group's table split into two tables with disjoint valid sets, run as
+    two grouped calls: the second merges into the first (forward) and adds to
+    it (backward, given the whole forward's O and LSE).  Against the oracle of
+    each group's whole table."""
+    from tests.test_accumulate_gpu import prefix_table, split
+    rng = random.Random(808)
+    Tq = Tk = 900
+    Hkv, G, d = 2, 2, 128
+    whole = [prefix_table(rng, Tq, 4), wl.varlen_slices([300, 600], ffa.CAUSAL)]
+    parts = [split(t, rng) for t in whole]
+    call = wl.Call(whole[0], Tq, Tk, Hkv * G, Hkv, d)
+    T = wl.make_tensors(call, 808)
+    q, k, v, do = (T[n].to(DEV) for n in ("q", "k", "v", "do"))
+    ends = [1, 2]
+    m1 = [ffa.build_meta(p[0], Tq, Tk, d) for p in parts]
+    m2 = [ffa.build_meta(p[1], Tq, Tk, d) for p in parts]
+    mw = [ffa.build_meta(t, Tq, Tk, d) for t in whole]
+    o, lse = ffa.fwd_grouped(q, k, v, m1, ends)
+    ffa.fwd_grouped(q, k, v, m2, ends, out=o, lse=lse, accumulate=True)
+    ow, lw = ffa.fwd_grouped(q, k, v, mw, ends)     # the whole forward for the backward
+    dq, dk, dv = ffa.bwd_grouped(q, k, v, ow, lw, do, m1, ends)
+    ffa.bwd_grouped(q, k, v, ow, lw, do, m2, ends, dq=dq, dk=dk, dv=dv, accumulate=True)
+    torch.cuda.synchronize()
+    for g, sl in enumerate(whole):
+        hq, hk = slice(g * G, g * G + G), slice(g, g + 1)
+        sub = {n: T[n][:, hq].contiguous() for n in ("q", "do")}
+        sub.update({n: T[n][:, hk].contiguous() for n in ("k", "v")})
+        o_ref, l_ref = orc.forward(sub["q"], sub["k"], sub["v"], sl)
+        check_o(o[:, hq], o_ref, f"merged O group {g}")
+        check_lse(lse[hq], l_ref, f"merged LSE group {g}")
+        g_ref = orc.backward(sub["q"], sub["k"], sub["v"], sub["do"], sl)
+        check_grad(dq[:, hq], g_ref[0], "dQ")
+        check_grad(dk[:, hk], g_ref[1], "dK")
+        check_grad(dv[:, hk], g_ref[2], "dV")
+
+
+def test_grouped_phases_match_one_call():
+    """PRE, DKDV and DQ as three grouped calls equal one grouped call."""
+    Tq = Tk = 700
+    tables = [wl.varlen_slices([200, 500], ffa.CAUSAL), [(0, 700, 0, 700, ffa.FULL)]]
+    call = wl.Call(tables[0], Tq, Tk, 8, 2, 128)
+    T = wl.make_tensors(call, 31)
+    q, k, v, do = (T[n].to(DEV) for n in ("q", "k", "v", "do"))
+    metas = [ffa.build_meta(t, Tq, Tk, 128) for t in tables]
+    o, lse = ffa.fwd_grouped(q, k, v, metas, [1, 2])
+    g1 = ffa.bwd_grouped(q, k, v, o, lse, do, metas, [1, 2])
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(ffa.bwd_workspace_size(q, k), dtype=torch.uint8, device=DEV)
+    for ph in (ffa.BWD_PRE, ffa.BWD_DKDV, ffa.BWD_DQ):
+        ffa.bwd_grouped(q, k, v, o, lse, do, metas, [1, 2], dq=dq, dk=dk, dv=dv, workspace=ws, phases=ph)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, (dq, dk, dv)):
+        rel = float((a.double() - b.double()).norm() / max(float(a.double().norm()), 1e-30))
+        assert rel <= 1e-3
