@@ -248,6 +248,16 @@ def test_varlen_causal_gqa_backward_full():
     check_grad(r["dv"], dv, "dV")
 
 
+def test_varlen_causal_head_dim_64_full():
+    """The 16K varlen-causal table at head_dim 64 (Hq 16, Hkv 8): every
+    element of O, LSE, dQ, dK, dV against the oracle."""
+    W = wl.workload(2)
+    c = wl.Call(W.calls[0].slices, 16384, 16384, 16, 8, 64)
+    T = wl.make_tensors(c, 64)
+    _say("16K varlen causal, d = 64: GPU then oracle")
+    full_check(c, T)
+
+
 def test_determinism_and_table_invariance():
     c, T, r = _cfg2()
     r2 = run(c, T)
