@@ -291,9 +291,43 @@ __global__ __launch_bounds__(NT, 3) __attribute__((amdgpu_waves_per_eu(3, 3))) v
     if (u + 1 < nU) stage_fn(std::integral_constant<int, 1>{}, u + 1);
   }
 
+  if ((a.flags & FFA_ACCUMULATE) == 0) {
+    // Plain store, staged through the idle tile ring so that each global
+    // store writes whole rows (as in the forward): wave wid stages its 32 rows
+    // at wid * 32 * RB, 16-byte chunk c of row r at chunk position c ^ (r % CPR).
+    constexpr int RB = D * 2, CPR = D / 8, RPI = 64 / CPR;
+    // the lane index is made opaque here so that the staging addresses are
+    // not computed before the stage loop and kept in registers through it
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int lr = ln & 31, lh = ln >> 5;
+    __attribute__((address_space(3))) char* wl = (__attribute__((address_space(3))) char*)smem + wid * 32 * RB;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf16x4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = static_cast<__bf16>(dqacc[mb][4 * j + i] * a.scale);
+        const int c = 4 * mb + j;
+        *reinterpret_cast<__attribute__((address_space(3))) bf16x4*>(
+            wl + lr * RB + ((c ^ (lr % CPR)) * 16) + 8 * lh) = w;
+      }
+    const int rsub = ln / CPR, ck = ln % CPR;
+#pragma unroll
+    for (int s = 0; s < 32 / RPI; ++s) {
+      const int r = RPI * s + rsub;
+      const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+          wl + r * RB + ((ck ^ (r % CPR)) * 16));
+      const int grow = m * BM_F + wid * 32 + r;
+      if (grow < a.Tq)
+        *reinterpret_cast<u32x4*>(a.dq + (int64_t)grow * a.dq_ts + (int64_t)head * a.dq_hs + 8 * ck) = v;
+    }
+    return;
+  }
   if (qok) {
     // FFA_ACCUMULATE: add to what dq holds (fp32 sum, one rounding)
-    const bool acc = (a.flags & FFA_ACCUMULATE) != 0;
+    const bool acc = true;
     __bf16* qp = a.dq + (int64_t)qrow * a.dq_ts + (int64_t)head * a.dq_hs;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)

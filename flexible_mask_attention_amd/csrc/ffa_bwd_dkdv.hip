@@ -301,9 +301,50 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
       }
   }
 
+  if ((a.flags & FFA_ACCUMULATE) == 0) {
+    // Plain store, staged through the idle tile ring so that each global
+    // store writes whole rows: wave wid stages its 32 keys' dK rows at
+    // wid * 32 * RB and their dV rows 32 KB further (d = 128; half that for
+    // d = 64), 16-byte chunk c of row r at chunk position c ^ (r % CPR).  Wave
+    // 0's region covers the split counter word, which that wave has read.
+    constexpr int RB = D * 2, CPR = D / 8, RPI = 64 / CPR, HALF = 4 * 32 * RB;
+    // opaque lane index: keeps the staging addresses out of the walk's registers
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int lr = ln & 31, lh = ln >> 5;
+    __attribute__((address_space(3))) char* wl = (__attribute__((address_space(3))) char*)smem + wid * 32 * RB;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf16x4 wk, wv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          wk[i] = static_cast<__bf16>(dkacc[mb][4 * j + i] * a.scale);
+          wv[i] = static_cast<__bf16>(dvacc[mb][4 * j + i]);
+        }
+        const int o = lr * RB + (((4 * mb + j) ^ (lr % CPR)) * 16) + 8 * lh;
+        *reinterpret_cast<__attribute__((address_space(3))) bf16x4*>(wl + o) = wk;
+        *reinterpret_cast<__attribute__((address_space(3))) bf16x4*>(wl + HALF + o) = wv;
+      }
+    const int rsub = ln / CPR, ck = ln % CPR;
+#pragma unroll
+    for (int s = 0; s < 32 / RPI; ++s) {
+      const int r = RPI * s + rsub;
+      const int o = r * RB + ((ck ^ (r % CPR)) * 16);
+      const u32x4 vk = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(wl + o);
+      const u32x4 vv = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(wl + HALF + o);
+      const int krow = n * BN_B + wid * 32 + r;
+      if (krow < a.Tk) {
+        *reinterpret_cast<u32x4*>(a.dk + (int64_t)krow * a.dk_ts + (int64_t)kvh * a.dk_hs + 8 * ck) = vk;
+        *reinterpret_cast<u32x4*>(a.dv + (int64_t)krow * a.dv_ts + (int64_t)kvh * a.dv_hs + 8 * ck) = vv;
+      }
+    }
+    return;
+  }
   if (kok) {
     // FFA_ACCUMULATE: add to what dk / dv hold (fp32 sum, one rounding)
-    const bool acc = (a.flags & FFA_ACCUMULATE) != 0;
+    const bool acc = true;
     __bf16* kp = a.dk + (int64_t)key * a.dk_ts + (int64_t)kvh * a.dk_hs;
     __bf16* vp = a.dv + (int64_t)key * a.dv_ts + (int64_t)kvh * a.dv_hs;
 #pragma unroll

@@ -212,6 +212,41 @@ void ffa_fwd_kernel(FwdArgs a) {
   // a row without valid keys in this call keeps its stored values.
   const bool acc = (a.flags & FFA_ACCUMULATE) != 0;
   const float l_tot = wave_swap_sum(l_run);
+  if (!acc) {
+    // Plain store: bf16(O / l) goes through the idle tile ring so that each
+    // global store writes whole rows (16 bytes per lane, 256 / D * 8 rows per
+    // instruction) instead of an 8-byte piece of 32 rows; the workgroup's slot
+    // is freed once its stores complete, so this shortens the gap before the
+    // next workgroup starts.  Wave wid stages its 32 rows at wid * 32 * RB;
+    // 16-byte chunk c of row r sits at chunk position c ^ (r % CPR).
+    constexpr int RB = D * 2, CPR = D / 8, RPI = 64 / CPR;
+    const float w_new = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (row0 < a.Tq && h32 == 0)
+      a.lse[(int64_t)head * a.Tq + row0] = l_tot > 0.f ? m_run * a.scale + logf(l_tot) : -INFINITY;
+    __attribute__((address_space(3))) char* wl = (__attribute__((address_space(3))) char*)smem + wid * 32 * RB;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf16x4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = static_cast<__bf16>(oacc[mb][4 * j + i] * w_new);
+        const int c = 4 * mb + j;
+        *reinterpret_cast<__attribute__((address_space(3))) bf16x4*>(
+            wl + l32 * RB + ((c ^ (l32 % CPR)) * 16) + 8 * h32) = w;
+      }
+    const int rsub = lane / CPR, ck = lane % CPR;
+#pragma unroll
+    for (int s = 0; s < 32 / RPI; ++s) {
+      const int r = RPI * s + rsub;
+      const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+          wl + r * RB + ((ck ^ (r % CPR)) * 16));
+      const int grow = m * BM_F + wid * RW + r;
+      if (grow < a.Tq)
+        *reinterpret_cast<u32x4*>(a.o + (int64_t)grow * a.o_ts + (int64_t)head * a.o_hs + 8 * ck) = v;
+    }
+    return;
+  }
   if (row0 < a.Tq) {
     float lse_new = l_tot > 0.f ? m_run * a.scale + logf(l_tot) : -INFINITY;
     float w_new = l_tot > 0.f ? 1.f / l_tot : 0.f, w_old = 0.f;
