@@ -327,15 +327,13 @@ __global__ __launch_bounds__(NT, 3) __attribute__((amdgpu_waves_per_eu(3, 3))) v
   }
   if (qok) {
     // FFA_ACCUMULATE: add to what dq holds (fp32 sum, one rounding)
-    const bool acc = true;
     __bf16* qp = a.dq + (int64_t)qrow * a.dq_ts + (int64_t)head * a.dq_hs;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         bf16x4* dst = reinterpret_cast<bf16x4*>(qp + 32 * mb + 8 * j + 4 * h32);
-        bf16x4 old = bf16x4{};
-        if (acc) old = *dst;
+        const bf16x4 old = *dst;
         bf16x4 w;
 #pragma unroll
         for (int i = 0; i < 4; ++i)

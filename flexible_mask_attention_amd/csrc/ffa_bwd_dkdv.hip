@@ -344,7 +344,6 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   }
   if (kok) {
     // FFA_ACCUMULATE: add to what dk / dv hold (fp32 sum, one rounding)
-    const bool acc = true;
     __bf16* kp = a.dk + (int64_t)key * a.dk_ts + (int64_t)kvh * a.dk_hs;
     __bf16* vp = a.dv + (int64_t)key * a.dv_ts + (int64_t)kvh * a.dv_hs;
 #pragma unroll
@@ -353,11 +352,7 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
       for (int j = 0; j < 4; ++j) {
         bf16x4* dk4 = reinterpret_cast<bf16x4*>(kp + 32 * mb + 8 * j + 4 * h32);
         bf16x4* dv4 = reinterpret_cast<bf16x4*>(vp + 32 * mb + 8 * j + 4 * h32);
-        bf16x4 ok = bf16x4{}, ov = bf16x4{};
-        if (acc) {
-          ok = *dk4;
-          ov = *dv4;
-        }
+        const bf16x4 ok = *dk4, ov = *dv4;
         bf16x4 wk, wv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
