@@ -136,6 +136,18 @@ def test_boundary_shapes(Tq, Tk, Hq, Hkv, d):
     full_check(c, wl.make_tensors(c, Tq + 7 * Tk))
 
 
+def test_multi_query_many_heads():
+    """One kv head shared by 32 query heads (multi-query attention): each dK/dV
+    step walks 32 query heads per tile, the split rule sees one kv head with
+    a very uneven causal walk, and the block map takes its non-multiple-of-8
+    kv-head path.  Varlen causal plus a FULL look-back slice, every output
+    against the oracle."""
+    sl = wl.varlen_slices([300, 500, 224], ffa.CAUSAL) + [(524, 1024, 0, 300, ffa.FULL)]
+    c = wl.Call(sl, 1024, 1024, 32, 1, 128)
+    _say(f"multi-query Hq=32 Hkv=1: {sl}")
+    full_check(c, wl.make_tensors(c, 77))
+
+
 def test_backward_phases_separately_match_one_call():
     """PRE, DKDV and DQ run as three calls (standalone row-statistics kernel)
     give the gradients of the single call (row statistics folded into dQ),
