@@ -148,6 +148,27 @@ def test_multi_query_many_heads():
     full_check(c, wl.make_tensors(c, 77))
 
 
+def test_one_long_causal_sequence_one_head():
+    """A single 8K causal sequence on one head pair: the first key blocks hold
+    far more than a resident workgroup's share of the backward, so the dK/dV
+    kernel splits its longest-first candidates into two halves (the fp32
+    partials meet through the workspace counters); run twice to check that the
+    counters are back at zero and the result is bitwise the same."""
+    T = 8192
+    c = wl.Call([(0, T, 0, T, ffa.CAUSAL)], T, T, 1, 1, 128)
+    _say("one long causal sequence T=8192 Hq=Hkv=1 d=128")
+    tens = wl.make_tensors(c, 88)
+    full_check(c, tens)
+    q, k, v, do = (tens[n].to(DEV) for n in ("q", "k", "v", "do"))
+    meta = ffa.build_meta(c.slices, T, T, c.d)
+    o, lse = ffa.fwd(q, k, v, meta)
+    g1 = ffa.bwd(q, k, v, o, lse, do, meta)
+    g2 = ffa.bwd(q, k, v, o, lse, do, meta)
+    torch.cuda.synchronize()
+    for a, b, n in zip(g1, g2, ("dQ", "dK", "dV")):
+        assert torch.equal(a, b), f"{n} differs between two identical calls"
+
+
 def test_backward_phases_separately_match_one_call():
     """PRE, DKDV and DQ run as three calls (standalone row-statistics kernel)
     give the gradients of the single call (row statistics folded into dQ),
