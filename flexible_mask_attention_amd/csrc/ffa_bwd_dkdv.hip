@@ -281,7 +281,10 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
       }
     __threadfence();
     __syncthreads();
-    int* flag = reinterpret_cast<int*>(smem);   // the tile ring is idle now
+    // the tile ring is idle now; the word sits past the output staging area
+    // below (2 x 4 x 32 rows of dK / dV), so no wave can overwrite it while
+    // another still reads it
+    int* flag = reinterpret_cast<int*>(smem + 2 * STAGE_B - 16);
     if (tid == 0) *flag = atomicAdd(a.split_cnt + (int64_t)cand * a.Hkv + kvh, 1);
     __syncthreads();
     if (*flag == 0) return;   // the other half finishes the block
@@ -305,9 +308,9 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     // Plain store, staged through the idle tile ring so that each global
     // store writes whole rows: wave wid stages its 32 keys' dK rows at
     // wid * 32 * RB and their dV rows 32 KB further (d = 128; half that for
-    // d = 64), 16-byte chunk c of row r at chunk position c ^ (r % CPR).  Wave
-    // 0's region covers the split counter word, which that wave has read.
+    // d = 64), 16-byte chunk c of row r at chunk position c ^ (r % CPR).
     constexpr int RB = D * 2, CPR = D / 8, RPI = 64 / CPR, HALF = 4 * 32 * RB;
+    static_assert(2 * HALF <= 2 * STAGE_B - 16, "output staging must not reach the split counter word");
     // opaque lane index: keeps the staging addresses out of the walk's registers
     int ln = lane;
     asm volatile("" : "+v"(ln));
