@@ -117,14 +117,20 @@ class GroupedCase:
         self.bwd()
 
 
-def phase_times(cases, reps):
-    """Average device time (ms) of each phase, from HIP events on the stream the
-    library launches on (torch's current stream)."""
-    # the backward runs as in a step: the dQ kernel with the row statistics
-    # folded in (PRE | DQ), then dK/dV
-    names = ["meta", "fwd", "bwd_dq", "bwd_dkdv"]
-    tot = {n: 0.0 for n in names}
-    for _ in range(reps):
+PHASES = ["meta", "fwd", "bwd_dq", "bwd_dkdv"]
+
+
+def phase_times(cases, min_reps, min_seconds=1.0):
+    """Device time (ms) of each phase per step, from HIP events recorded on the
+    stream the library launches on (torch's current stream), over at least
+    ``min_reps`` repetitions and ``min_seconds`` of device time.  The backward
+    runs as in a step: the dQ kernel with the row statistics folded in
+    (PRE | DQ), then dK/dV.  Returns per phase the mean, median, first and
+    third quartile and the number of samples."""
+    samples = {n: [] for n in PHASES}
+    total, reps = 0.0, 0
+    while reps < min_reps or total < 1e3 * min_seconds:
+        rep = {n: 0.0 for n in PHASES}
         for cs in cases:
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
             ev[0].record()
@@ -137,9 +143,43 @@ def phase_times(cases, reps):
             cs.bwd(ffa.BWD_DKDV)
             ev[4].record()
             torch.cuda.synchronize()
-            for i, n in enumerate(names):
-                tot[n] += ev[i].elapsed_time(ev[i + 1])
-    return {n: tot[n] / reps for n in names}
+            for i, n in enumerate(PHASES):
+                rep[n] += ev[i].elapsed_time(ev[i + 1])
+        for n in PHASES:
+            samples[n].append(rep[n])
+        total += sum(rep.values())
+        reps += 1
+    out = {}
+    for n in PHASES:
+        x = sorted(samples[n])
+        q = lambda f: x[min(len(x) - 1, int(round(f * (len(x) - 1))))]   # noqa: E731
+        out[n] = {"mean": sum(x) / len(x), "median": q(0.5), "q1": q(0.25), "q3": q(0.75), "n": len(x)}
+    return out
+
+
+def gemm_ceiling(dev, n=8192, reps=20):
+    """Dense bf16 GEMM throughput of the platform library (torch.matmul, which
+    dispatches to hipBLASLt) at n^3, timed with HIP events: context for the
+    kernels' fraction of the published peak, not a denominator."""
+    a = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    b = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    for _ in range(5):
+        torch.matmul(a, b)
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.matmul(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    times.sort()
+    med = times[len(times) // 2]
+    tf = 2.0 * n ** 3 / (med * 1e-3) / 1e12
+    del a, b
+    torch.cuda.empty_cache()
+    return {"tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4), "shape": f"{n}^3 bf16",
+            "library": "torch.matmul (hipBLASLt)", "stat": f"median of {reps}"}
 
 
 def source_code_digest(csrc):
@@ -213,12 +253,24 @@ def profile_phase(cases, phase, reps):
     log(f"profiled phase {phase}: {reps} launch(es) per call")
 
 
+def host_threads():
+    """Threads for the oracle leg: the cores this process may run on
+    (affinity), capped by OMP_NUM_THREADS when the environment sets it (the
+    host's share of cores per GPU)."""
+    aff = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    n = min(aff, int(env)) if env.isdigit() and int(env) > 0 else aff
+    return n, aff
+
+
 def cpu_baseline(call, seed, area, min_seconds=10.0):
     """The fp64 oracle, untuned, timed on the host cores: forward + backward of
     the whole workload (all heads, full mask), repeated until at least
     ``min_seconds`` have passed.  Inputs are the CPU-seeded tensors of the
     same shapes."""
     from oracle import ffa_oracle as orc
+    threads, aff = host_threads()
+    torch.set_num_threads(threads)
     T = wl.make_tensors(call, seed)
     reps, t0 = 0, time.perf_counter()
     while True:
@@ -230,7 +282,7 @@ def cpu_baseline(call, seed, area, min_seconds=10.0):
             break
     f = 4.0 * call.d * area * call.Hq * 3.5 * reps
     return {"value": round(f / dt / 1e12, 4), "unit": "TFLOP/s", "cores": torch.get_num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "affinity_cores": aff, "blas_threads": torch.get_num_threads(),
             "sample": f"whole workload (all {call.Hq} query heads, full mask), fwd + bwd, "
                       f"{reps} pass(es) in {dt:.1f} s"}
 
@@ -242,6 +294,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2, help="1..5 (see workloads.py)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gemm-ceiling", action="store_true")
+    ap.add_argument("--min-time", type=float, default=1.0,
+                    help="seconds of device time over which per-phase medians are taken")
     ap.add_argument("--profile-phase", default=None,
                     help="meta|fwd|bwd_dkdv|bwd_dq|copy: only launch that phase --reps times "
                          "(for hardware-counter runs); prints no JSON")
@@ -287,7 +342,8 @@ def main():
     torch.cuda.synchronize()
     step_s = (time.perf_counter() - t0) / args.steps
 
-    ph = phase_times(cases, max(5, args.steps // 2))
+    stats = phase_times(cases, max(20, args.steps // 2), args.min_time)
+    ph = {n: stats[n]["median"] for n in PHASES}
     t_fwd = ph["fwd"] * 1e-3
     t_bwd = (ph["bwd_dkdv"] + ph["bwd_dq"]) * 1e-3
     # algorithmic FLOPs per kernel: fwd 4d per valid pair and head; of the
@@ -297,10 +353,15 @@ def main():
     kernels = {}
     for n in ("fwd", "bwd_dkdv", "bwd_dq"):
         tf = alg[n] / (ph[n] * 1e-3) / 1e12
-        kernels[n] = {"ms": round(ph[n], 4), "tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
-    kernels["meta"] = {"ms": round(ph["meta"], 4)}
+        st = stats[n]
+        kernels[n] = {"ms": round(ph[n], 4), "tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                      "ms_mean": round(st["mean"], 4), "ms_iqr": [round(st["q1"], 4), round(st["q3"], 4)]}
+    kernels["meta"] = {"ms": round(ph["meta"], 4),
+                       "ms_iqr": [round(stats["meta"]["q1"], 4), round(stats["meta"]["q3"], 4)]}
+    # roofline of the dominant kernel: algorithmic FLOPs per launch over its
+    # average launch duration
     dom = max(("fwd", "bwd_dkdv", "bwd_dq"), key=lambda n: ph[n])
-    achieved = kernels[dom]["tflops"]
+    achieved = round(alg[dom] / (stats[dom]["mean"] * 1e-3) / 1e12, 1)
     roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": recorded_traffic(dom, W.name), "traffic_unit": "HBM bytes per launch"}
@@ -323,9 +384,14 @@ def main():
         "fwd_pct_peak": round(100 * f_fwd / t_fwd / 1e12 / PEAK_BF16_TFLOPS, 2),
         "bwd_tflops": round(f_bwd / t_bwd / 1e12, 1),
         "bwd_pct_peak": round(100 * f_bwd / t_bwd / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "timing": {"stat": "median over HIP-event samples per phase, IQR alongside",
+                   "samples": stats["fwd"]["n"],
+                   "seconds": round(sum(stats[n]["mean"] for n in PHASES) * stats["fwd"]["n"] * 1e-3, 2)},
         "kernels": kernels,
         "roofline": roofline,
     }
+    if not args.no_gemm_ceiling:
+        out["gemm_ceiling"] = gemm_ceiling(dev)
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(c0, W.seed, areas[0])

@@ -138,10 +138,53 @@ def _tout(t: torch.Tensor) -> TensorOut:
 
 
 def _check_thd(t: torch.Tensor, name: str):
-    if t.dtype != torch.bfloat16 or t.dim() != 3 or not t.is_cuda:
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or t.dim() != 3 or not t.is_cuda:
         raise FFAError(f"{name} must be a 3-D bfloat16 CUDA tensor [tokens, heads, head_dim]")
     if t.stride(2) != 1:
         raise FFAError(f"{name}: the head_dim axis must be contiguous")
+
+
+def _check_like(t: torch.Tensor, like: torch.Tensor, name: str, like_name: str):
+    """``t`` (a caller-given output or a second input) must be a THD bf16 tensor
+    of ``like``'s shape on ``like``'s device: the kernels write / read it with
+    ``like``'s extents."""
+    _check_thd(t, name)
+    if tuple(t.shape) != tuple(like.shape) or t.device != like.device:
+        raise FFAError(f"{name} must have the shape {tuple(like.shape)} and device of {like_name}, "
+                       f"got {tuple(t.shape)} on {t.device}")
+
+
+def _check_lse(lse: torch.Tensor, q: torch.Tensor, name: str = "lse"):
+    """The LSE buffer: float32 [Hq, Tq], contiguous, on q's device."""
+    want = (q.shape[1], q.shape[0])
+    if (not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32 or tuple(lse.shape) != want
+            or not lse.is_contiguous() or lse.device != q.device):
+        got = (tuple(lse.shape), lse.dtype, lse.device) if isinstance(lse, torch.Tensor) else type(lse)
+        raise FFAError(f"{name} must be a contiguous float32 tensor of shape {want} on {q.device}, got {got}")
+
+
+def _check_inputs(q, k, v, extra=()):
+    """q [Tq,Hq,d] and k, v [Tk,Hkv,d] on one device, plus (tensor, name) pairs
+    shaped like q (o, do)."""
+    _check_thd(q, "q")
+    _check_thd(k, "k")
+    _check_like(v, k, "v", "k")
+    if k.device != q.device or k.shape[2] != q.shape[2]:
+        raise FFAError("q and k must share the device and head_dim")
+    for t, n in extra:
+        _check_like(t, q, n, "q")
+
+
+def _check_meta(meta, q, k, name="meta"):
+    """The metadata must be built for this call's sequence lengths and head_dim
+    (the kernels would otherwise write nothing) and live on q's device."""
+    if not isinstance(meta, BlockMeta):
+        raise FFAError(f"{name} must be a BlockMeta from build_meta")
+    if (meta.seqlen_q, meta.seqlen_k, meta.head_dim) != (q.shape[0], k.shape[0], q.shape[2]):
+        raise FFAError(f"{name} was built for seqlen_q={meta.seqlen_q}, seqlen_k={meta.seqlen_k}, "
+                       f"head_dim={meta.head_dim}; the tensors have {q.shape[0]}, {k.shape[0]}, {q.shape[2]}")
+    if meta.buf.device != q.device:
+        raise FFAError(f"{name} lives on {meta.buf.device}, the tensors on {q.device}")
 
 
 class BlockMeta:
@@ -212,14 +255,21 @@ def meta_workspace_size(num_slices: int, seqlen_q: int, seqlen_k: int, head_dim:
 
 
 def build_meta(slices, seqlen_q: int, seqlen_k: int, head_dim: int, device=None,
-               stream=None, out: Optional[torch.Tensor] = None) -> BlockMeta:
+               stream=None, out: Optional[torch.Tensor] = None, validate: bool = True) -> BlockMeta:
     """Build block metadata for a slice table.
 
     ``slices``: sequence of (q_start, q_end, k_start, k_end, mask_type) or an
     int32 tensor [S, 5] (host or device).  The buffer is sized from the host
     copy of the table when one is available; ``out`` (uint8, 256-byte aligned)
     is used as given, and the device status word reports a table that does
-    not fit in it."""
+    not fit in it.
+
+    ``validate`` (default): read the device status word once the build is done
+    (a synchronising read, paid once per mask since the metadata is reused)
+    and raise FFAError for a bad table, so that no forward or backward can run
+    on metadata that makes the kernels write nothing.  Pass False where no
+    synchronisation is allowed (e.g. under graph capture); the caller then
+    checks ``status()`` itself."""
     if isinstance(slices, torch.Tensor):
         t = slices.to(torch.int32).reshape(-1, 5)
     else:
@@ -235,6 +285,13 @@ def build_meta(slices, seqlen_q: int, seqlen_k: int, head_dim: int, device=None,
                                       out.data_ptr(), out.numel(), _stream(stream)), "ffa_build_block_meta")
     m = BlockMeta(out, S, seqlen_q, seqlen_k, head_dim)
     m._slices = d_slices      # keep the device table alive with the metadata
+    if validate:
+        st = m.status()
+        if st != 0:
+            names = [n for f, n in ((META_ERR_BOUNDS, "range out of bounds"), (META_ERR_TYPE, "unknown mask type"),
+                                    (META_ERR_OVERLAP, "overlapping slices"),
+                                    (META_ERR_CAPACITY, "metadata buffer too small")) if st & f]
+            raise FFAError(f"bad slice table (status {st}: {', '.join(names)})")
     return m
 
 
@@ -253,22 +310,26 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, meta: BlockMeta, scal
     ``accumulate``: merge into the (out, lse) given (ffa_fwd_ex with FFA_ACCUMULATE)."""
     if accumulate and (out is None or lse is None):
         raise FFAError("accumulate needs the previous out and lse")
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _check_thd(t, n)
+    _check_inputs(q, k, v)
+    _check_meta(meta, q, k)
     sh = _shape(q, k, scale)
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    _check_like(out, q, "out", "q")
     if lse is None:
         lse = torch.empty(q.shape[1], q.shape[0], dtype=torch.float32, device=q.device)
+    _check_lse(lse, q)
     _check(lib().ffa_fwd_ex(ctypes.byref(sh), _tin(q), _tin(k), _tin(v), meta.ptr, _tout(out),
                             lse.data_ptr(), ACCUMULATE if accumulate else 0, _stream(stream)),
            "ffa_fwd_ex")
     return out, lse
 
 
-def _groups(metas, kv_head_end, Hkv):
+def _groups(metas, kv_head_end, q, k):
     if len(metas) != len(kv_head_end) or not 1 <= len(metas) <= MAX_MASK_GROUPS:
         raise FFAError("need 1..8 metadata buffers, one per kv-head group")
+    for i, m in enumerate(metas):
+        _check_meta(m, q, k, f"metas[{i}]")
     ptrs = (ctypes.c_void_p * len(metas))(*[m.ptr for m in metas])
     ends = (ctypes.c_int32 * len(metas))(*[int(e) for e in kv_head_end])
     return len(metas), ptrs, ends
@@ -280,13 +341,14 @@ def fwd_grouped(q, k, v, metas: Sequence[BlockMeta], kv_head_end: Sequence[int],
     kv_head_end[g]) and their query heads use metas[g] (ffa_fwd_grouped)."""
     if accumulate and (out is None or lse is None):
         raise FFAError("accumulate needs the previous out and lse")
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _check_thd(t, n)
+    _check_inputs(q, k, v)
     sh = _shape(q, k, scale)
-    ng, ptrs, ends = _groups(metas, kv_head_end, k.shape[1])
+    ng, ptrs, ends = _groups(metas, kv_head_end, q, k)
     out = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
+    _check_like(out, q, "out", "q")
     if lse is None:
         lse = torch.empty(q.shape[1], q.shape[0], dtype=torch.float32, device=q.device)
+    _check_lse(lse, q)
     _check(lib().ffa_fwd_grouped(ctypes.byref(sh), _tin(q), _tin(k), _tin(v), ng, ptrs, ends,
                                  _tout(out), lse.data_ptr(), ACCUMULATE if accumulate else 0,
                                  _stream(stream)), "ffa_fwd_grouped")
@@ -299,16 +361,12 @@ def bwd_grouped(q, k, v, o, lse, do, metas: Sequence[BlockMeta], kv_head_end: Se
     """Backward of a grouped forward (ffa_bwd_grouped) -> (dq, dk, dv)."""
     if accumulate and (dq is None or dk is None or dv is None):
         raise FFAError("accumulate needs the dq, dk, dv to add to")
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
-        _check_thd(t, n)
+    _check_inputs(q, k, v, ((o, "o"), (do, "do")))
+    _check_lse(lse, q)
     sh = _shape(q, k, scale)
-    ng, ptrs, ends = _groups(metas, kv_head_end, k.shape[1])
-    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
-    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
-    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
-    need = bwd_workspace_size(q, k, scale)
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    ng, ptrs, ends = _groups(metas, kv_head_end, q, k)
+    dq, dk, dv = _grad_buffers(q, k, v, dq, dk, dv)
+    workspace = _workspace(q, k, scale, workspace)
     _check(lib().ffa_bwd_grouped(ctypes.byref(sh), _tin(q), _tin(k), _tin(v), _tin(o), lse.data_ptr(),
                                  _tin(do), ng, ptrs, ends, _tout(dq), _tout(dk), _tout(dv),
                                  workspace.data_ptr(), workspace.numel(), int(phases),
@@ -373,6 +431,26 @@ def bwd_workspace_size(q, k, scale=None) -> int:
     return n.value
 
 
+def _grad_buffers(q, k, v, dq, dk, dv):
+    """Caller-given gradient buffers (checked against q, k, v) or new ones."""
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+    _check_like(dq, q, "dq", "q")
+    _check_like(dk, k, "dk", "k")
+    _check_like(dv, v, "dv", "v")
+    return dq, dk, dv
+
+
+def _workspace(q, k, scale, workspace):
+    need = bwd_workspace_size(q, k, scale)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    elif workspace.device != q.device or not workspace.is_contiguous():
+        raise FFAError(f"workspace must be a contiguous buffer on {q.device}")
+    return workspace
+
+
 def bwd(q, k, v, o, lse, do, meta: BlockMeta, scale: float = None, dq=None, dk=None, dv=None,
         workspace: Optional[torch.Tensor] = None, stream=None, phases: int = BWD_ALL,
         accumulate: bool = False):
@@ -381,15 +459,12 @@ def bwd(q, k, v, o, lse, do, meta: BlockMeta, scale: float = None, dq=None, dk=N
     ``accumulate`` adds to the dq, dk, dv given (ffa_bwd_ex with FFA_ACCUMULATE)."""
     if accumulate and (dq is None or dk is None or dv is None):
         raise FFAError("accumulate needs the dq, dk, dv to add to")
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
-        _check_thd(t, n)
+    _check_inputs(q, k, v, ((o, "o"), (do, "do")))
+    _check_lse(lse, q)
+    _check_meta(meta, q, k)
     sh = _shape(q, k, scale)
-    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
-    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
-    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
-    need = bwd_workspace_size(q, k, scale)
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = _grad_buffers(q, k, v, dq, dk, dv)
+    workspace = _workspace(q, k, scale, workspace)
     _check(lib().ffa_bwd_ex(ctypes.byref(sh), _tin(q), _tin(k), _tin(v), _tin(o), lse.data_ptr(),
                             _tin(do), meta.ptr, _tout(dq), _tout(dk), _tout(dv), workspace.data_ptr(),
                             workspace.numel(), int(phases), ACCUMULATE if accumulate else 0,

@@ -36,8 +36,10 @@ bool check_tensor(const void* p, int64_t ts, int64_t hs, int64_t T, int64_t H, i
   if (T == 0) return true;
   if (!p || !aligned(p, 16)) return false;
   if (ts < 0 || hs < 0 || ts % 8 || hs % 8) return false;
-  // tiles are read through buffer descriptors spanning up to 128 token rows
-  if (T > 1 && (ts < D || ts >= (1LL << 23))) return false;
+  // tiles are read through buffer descriptors whose range is the tile's
+  // valid rows times the token stride (up to 128 rows): a stride below
+  // head_dim would cut a row short even for a single token
+  if (ts < D || ts >= (1LL << 23)) return false;
   (void)H;
   return true;
 }

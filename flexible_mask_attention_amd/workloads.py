@@ -217,3 +217,27 @@ def random_slices(rng: random.Random, Tq: int, Tk: int, n: int, types=(0, 1, 2, 
         k1 = rng.randint(k0 + 1, Tk)
         out.append((q0, q1, k0, k1, rng.choice(types)))
     return out
+
+
+def random_banded_slices(rng: random.Random, Tq: int, Tk: int, bands: int = 3,
+                         per_band=(2, 4), types=(0, 1, 2, 3)) -> List[Slice]:
+    """Random *disjoint* slice table with several slices on one query row: the
+    query axis is cut into ``bands`` bands, and each band gets 2-4 slices with
+    pairwise disjoint key ranges (so their valid sets cannot overlap) and
+    random types, each over a random sub-range of the band's queries.  A row
+    then attends to the union of several slices' keys, which the kernels
+    combine bit by bit per tile."""
+    cuts = sorted(rng.sample(range(1, Tq), min(bands - 1, Tq - 1))) if bands > 1 else []
+    bounds = [0] + cuts + [Tq]
+    out: List[Slice] = []
+    for q0, q1 in zip(bounds[:-1], bounds[1:]):
+        n = rng.randint(per_band[0], per_band[1])
+        n = min(n, Tk // 2)
+        if n < 1:
+            continue
+        pts = sorted(rng.sample(range(0, Tk + 1), 2 * n))
+        for i in range(n):
+            a, z = rng.randint(q0, q1 - 1), rng.randint(q0 + 1, q1)
+            qa, qz = min(a, z - 1), max(a + 1, z)
+            out.append((qa, qz, pts[2 * i], pts[2 * i + 1], rng.choice(types)))
+    return out

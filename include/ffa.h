@@ -37,7 +37,11 @@
  *    failed launch returns FFA_ERR_HIP.  Problems in the device-resident slice
  *    table are found by ffa_build_block_meta on the device and recorded in the
  *    metadata's status word (FFA_META_ERR_* flags); ffa_fwd and ffa_bwd then
- *    write nothing.  No function throws.
+ *    write nothing.  The same holds when the metadata was built for other
+ *    sequence lengths than the call's seqlen_q / seqlen_k (the kernels compare
+ *    them with the metadata header on the device): outputs are left as they
+ *    were, so a caller that cannot rule this out reads the status word (or
+ *    pre-fills its outputs) before trusting them.  No function throws.
  */
 #ifndef FFA_H_
 #define FFA_H_
@@ -82,7 +86,7 @@ typedef enum {
 typedef struct {
   const void* ptr;       /* device, 16-byte aligned */
   int64_t token_stride;  /* elements between consecutive tokens: multiple of 8,
-                            >= head_dim and < 2^23 when there is more than one token */
+                            >= head_dim and < 2^23 for every tensor with a token */
   int64_t head_stride;   /* elements between consecutive heads (multiple of 8) */
 } ffa_tensor_in;
 
@@ -153,28 +157,56 @@ FFA_API ffa_status ffa_build_block_meta(const int32_t* d_slices, int32_t num_sli
                                         int32_t seqlen_q, int32_t seqlen_k, int32_t head_dim,
                                         void* d_meta, size_t meta_bytes, void* stream);
 
-/* Fill *out from the layout of a metadata buffer built with these arguments. */
+/* Fill *out from the layout of a metadata buffer built with these arguments:
+ * host pointer arithmetic only, no device access.  The fields are the block
+ * classes and CSR lists of the MagiAttention documentation page ("FFA_FA4"
+ * optimisations, item 1: Full / Partial / Empty tiles from create_block_mask,
+ * a tile out of bounds only in q counted as Full; item 2: full_block_offset /
+ * mask_block_offset CSR lists).  d_meta is not read; out receives device
+ * pointers into it.  Bad sizes give FFA_ERR_INVALID_ARGUMENT, a head_dim other
+ * than 64 or 128 FFA_ERR_UNSUPPORTED. */
 FFA_API ffa_status ffa_block_meta_view(const void* d_meta, int32_t num_slices, int32_t seqlen_q,
                                        int32_t seqlen_k, int32_t head_dim,
                                        ffa_block_meta_view_t* out);
 
 /* Forward: o = softmax(scale * q k^T restricted to the valid set) v and lse,
- * computed with an online softmax over the q2k Full and Partial tiles of
- * each query block (per-element masking only on Partial tiles).
- * o: bf16 like q.  lse: device fp32 [num_heads_q][seqlen_q], 16-byte aligned.
- * Rows with no valid key get o = 0, lse = -inf. */
+ * the FFA forward kernel of the MagiAttention blog deep-dive (section
+ * "Flex-Flash-Attention 与 AttnSlice": the AttnSlice equation defines the valid
+ * set as the union of the slices' masks, Fig. 5 the per-slice data loading and
+ * on-chip compute), computed with an online softmax over the q2k Full and
+ * Partial tiles of each query block, per-element masking only on Partial tiles
+ * (documentation page, "FFA_FA4" items 1 and 2).
+ * q: [seqlen_q][num_heads_q][head_dim] bf16; k, v: [seqlen_k][num_heads_kv][head_dim]
+ * bf16 (read only).  d_meta: built by ffa_build_block_meta for this seqlen_q,
+ * seqlen_k (read only).  o: bf16 like q, written.  lse: device fp32
+ * [num_heads_q][seqlen_q], 16-byte aligned, written.  Rows with no valid key
+ * get o = 0, lse = -inf.  Errors as in the conventions above. */
 FFA_API ffa_status ffa_fwd(const ffa_shape* shape, ffa_tensor_in q, ffa_tensor_in k,
                            ffa_tensor_in v, const void* d_meta, ffa_tensor_out o, float* lse,
                            void* stream);
 
-/* Scratch bytes ffa_bwd needs: per (query head, row) the dot product
- * -D_i = -(dO_i . O_i) and LSE_i * log2(e), both fp32; then, for the dK/dV
- * load balance, finish counters and fp32 partial dK, dV of the longest key
- * blocks of each kv head (up to min(32, max(4, 128 / num_heads_kv)) blocks of
- * 128 keys, two halves each).  Depends on the shape only. */
+/* Scratch bytes ffa_bwd needs for the backward of the FFA kernel (MagiAttention
+ * blog deep-dive, section "Flex-Flash-Attention 与 AttnSlice", Fig. 5: the
+ * backward merges partial results; here the only partials are those of split
+ * key blocks, see ffa_bwd).  Layout, each region starting at a 256-byte
+ * boundary of d_ws:
+ *   -D_i = -(dO_i . O_i)      fp32 [num_heads_q][seqlen_q]
+ *   LSE_i * log2(e)           fp32 [num_heads_q][seqlen_q]
+ *   split finish counters     int32 [E][num_heads_kv]
+ *   split partial dK, dV      fp32 [E][num_heads_kv][2 halves][dK, dV][128 * head_dim]
+ * with E = min(ceil(seqlen_k / 128), min(32, max(4, 128 / num_heads_kv))) key
+ * blocks of 128 keys per kv head (the longest ones).  Depends on the shape only.
+ * Bad shapes give FFA_ERR_INVALID_ARGUMENT / FFA_ERR_UNSUPPORTED; null bytes
+ * FFA_ERR_INVALID_ARGUMENT. */
 FFA_API ffa_status ffa_bwd_workspace_size(const ffa_shape* shape, size_t* bytes);
 
-/* Backward: dq, dk, dv of the forward above, given its o and lse.
+/* Backward: dq, dk, dv of the forward above, given its o and lse: the textbook
+ * gradient of the FFA forward (MagiAttention blog deep-dive, section
+ * "Flex-Flash-Attention 与 AttnSlice", Fig. 5: FFA forward and backward
+ * kernels over the slices; documentation page, "FFA_FA4" items 1 and 2 for
+ * the k2q / q2k tile lists it walks).  q, k, v, o, dout as for ffa_fwd (dout
+ * like o); lse as written by ffa_fwd (read only); dq like q, dk and dv like k,
+ * all bf16 and written.
  * dk and dv are accumulated per key block in a fixed order over the k2q tiles
  * and the query heads that share the key head, and dq per query block over
  * its q2k tiles.  A key block whose work exceeds an even share of the
@@ -197,7 +229,9 @@ FFA_API ffa_status ffa_bwd(const ffa_shape* shape, ffa_tensor_in q, ffa_tensor_i
 #define FFA_BWD_DQ 4    /* dq (reads D from d_ws)                                 */
 #define FFA_BWD_ALL 7
 
-/* ffa_bwd restricted to a subset of its phases (bitwise OR of FFA_BWD_*).
+/* ffa_bwd restricted to a subset of its phases (bitwise OR of FFA_BWD_*), the
+ * same backward of the FFA kernel (blog deep-dive, "Flex-Flash-Attention 与
+ * AttnSlice", Fig. 5) split where its kernels meet; arguments as for ffa_bwd.
  * DKDV and DQ read the values that PRE wrote into the same d_ws; once PRE has
  * finished they are independent of each other, so a caller may run them on
  * two streams.  When PRE and DQ are requested together, the dQ kernel

@@ -531,6 +531,54 @@ def backward_dq_rows(q, k, v, do, slices: Sequence, rows, scale: float = None,
     return forward_backward_rows(q, k, v, do, slices, rows, scale, max_elems)[2]
 
 
+def backward_keys(q, k, v, do, slices: Sequence, keys, scale: float = None, kv_heads=None,
+                  max_elems: int = 1 << 25, progress=None):
+    """dK and dV for the given key rows only, of the listed kv heads (default:
+    all of them) with all their query heads: the gradient of ``backward``
+    restricted to the columns j in ``keys``,
+      dK_j = scale sum_{h in group} sum_i dS_ij q_i,
+      dV_j = sum_{h in group} sum_i P_ij dO_i,
+      P_ij = exp(s_ij - LSE_i),  dS_ij = P_ij (dO_i . v_j - D_i),  D_i = dO_i . O_i.
+    P needs the LSE of each row over all of its valid keys and D needs the
+    row's whole O, so every row is evaluated as in ``forward`` (two-pass, over
+    the key window of its batch); only the listed columns enter the sums.
+    ``progress`` (optional) is called with a short text after each kv head.
+    Returns dK, dV [len(keys), len(kv_heads), d] (float64 ndarrays)."""
+    import torch
+    Tq, Hq, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    keys = np.asarray(keys, dtype=np.int64)
+    heads = list(range(Hkv)) if kv_heads is None else [int(g) for g in kv_heads]
+    order = np.argsort(keys, kind="stable")
+    skeys = keys[order]
+    batches = list(_row_batches(np.arange(Tq), slices, max(1, max_elems // G)))
+    dK = torch.zeros(len(keys), len(heads), d, dtype=torch.float64)
+    dV = torch.zeros(len(keys), len(heads), d, dtype=torch.float64)
+    for gi, g in enumerate(heads):
+        hs = slice(g * G, (g + 1) * G)
+        for a, b, w0, w1, mask in batches:
+            lo, hi = np.searchsorted(skeys, [w0, w1])
+            if w1 <= w0 or lo == hi:
+                continue                      # no listed key in this batch's window
+            pos = torch.from_numpy(order[lo:hi])          # output rows of those keys
+            cols = torch.from_numpy(skeys[lo:hi] - w0)    # their window columns
+            Qb, dOb = _f64(q[a:b, hs, :]), _f64(do[a:b, hs, :])
+            Kw, Vw = _f64(k[w0:w1, g, :]), _f64(v[w0:w1, g, :])
+            _, P, Ob = _attend(Qb, Kw, Vw, torch.from_numpy(mask), scale)
+            B = b - a
+            D = (dOb * Ob).sum(dim=-1, keepdim=True)                         # [B, G, 1]
+            Ps = P[:, :, cols]                                                # [B, G, n]
+            dS = Ps * ((dOb.reshape(B * G, d) @ Vw[cols].T).view(B, G, -1) - D)
+            dK[pos, gi, :] += scale * (dS.reshape(B * G, -1).T @ Qb.reshape(B * G, d))
+            dV[pos, gi, :] += Ps.reshape(B * G, -1).T @ dOb.reshape(B * G, d)
+        if progress is not None:
+            progress(f"kv head {g}: {len(keys)} keys done")
+    return dK.numpy(), dV.numpy()
+
+
 def lse_merge(o1, lse1, o2, lse2):
     """Merge two partial attentions over disjoint key sets (same rows):
     LSE = logaddexp(LSE1, LSE2), O = e^{LSE1-LSE} O1 + e^{LSE2-LSE} O2.

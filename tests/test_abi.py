@@ -38,6 +38,7 @@ def test_abi_version_and_strings():
     assert L.ffa_abi_version() == 4
     for code in range(6):
         assert len(L.ffa_status_string(code)) > 0
+    assert L.ffa_status_string(99) == b"unknown status"
 
 
 def _shape(Tq=256, Tk=256, Hq=2, Hkv=2, d=64, scale=0.125):
@@ -61,6 +62,29 @@ def test_host_validation_returns_before_enqueue():
     assert L.ffa_fwd(P(_shape(scale=-0.5)), good, good, good, meta, goodo, lse, None) == 1
     # token stride below head_dim
     assert L.ffa_fwd(P(_shape()), ffa.TensorIn(0x1000, 32, 64), good, good, meta, goodo, lse, None) == 1
+    # ... also for a single token: its tile is read through a buffer range of
+    # valid rows x token stride, which a short stride (0 from expand) would cut
+    one_q, one_k = _shape(Tq=1), _shape(Tk=1)
+    short = ffa.TensorIn(0x1000, 0, 64)
+    short_o = ffa.TensorOut(0x1000, 8, 64)
+    assert L.ffa_fwd(P(one_q), short, good, good, meta, goodo, lse, None) == 1
+    assert L.ffa_fwd(P(one_q), good, good, good, meta, short_o, lse, None) == 1
+    assert L.ffa_fwd(P(one_k), good, short, good, meta, goodo, lse, None) == 1
+    assert L.ffa_fwd(P(one_k), good, good, short, meta, goodo, lse, None) == 1
+    ws_big = 1 << 30
+    assert L.ffa_bwd(P(one_q), good, good, good, good, lse, short, meta, goodo, goodo, goodo,
+                     0x100000, ws_big, None) == 1
+    assert L.ffa_bwd(P(one_q), good, good, good, short, lse, good, meta, goodo, goodo, goodo,
+                     0x100000, ws_big, None) == 1
+    assert L.ffa_bwd(P(one_q), good, good, good, good, lse, good, meta, short_o, goodo, goodo,
+                     0x100000, ws_big, None) == 1
+    assert L.ffa_bwd(P(one_k), good, short, good, good, lse, good, meta, goodo, goodo, goodo,
+                     0x100000, ws_big, None) == 1
+    assert L.ffa_bwd(P(one_k), good, good, good, good, lse, good, meta, goodo, short_o, goodo,
+                     0x100000, ws_big, None) == 1
+    assert L.ffa_bwd(P(one_k), good, good, good, good, lse, good, meta, goodo, goodo, short_o,
+                     0x100000, ws_big, None) == 1
+    assert L.ffa_fwd(P(_shape(Tq=1)), ffa.TensorIn(0x1000, 1 << 23, 64), good, good, meta, goodo, lse, None) == 1
     # null / misaligned tensor pointers, bad strides
     assert L.ffa_fwd(P(_shape()), ffa.TensorIn(0, 128, 64), good, good, meta, goodo, lse, None) == 1
     assert L.ffa_fwd(P(_shape()), ffa.TensorIn(0x1002, 128, 64), good, good, meta, goodo, lse, None) == 1

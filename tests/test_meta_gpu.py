@@ -30,7 +30,7 @@ def _expected_slice_lists(slices, Tq, Tk, BM):
 
 
 def check_meta(slices, Tq, Tk, d=128, meta=None):
-    m = meta if meta is not None else ffa.build_meta(slices, Tq, Tk, d)
+    m = meta if meta is not None else ffa.build_meta(slices, Tq, Tk, d, validate=False)
     csr = m.csr()
     BMf, BNf, BMb, BNb = csr["tiles"]
     assert m.status() == orc.validate(slices, Tq, Tk)
@@ -111,7 +111,7 @@ def test_meta_status_flags():
     need = ffa.meta_workspace_size(len(sl), 16384, 16384, 128, torch.tensor(sl, dtype=torch.int32))
     fixed = ffa.meta_workspace_size(len(sl), 16384, 16384, 128, torch.zeros(len(sl), 5, dtype=torch.int32))
     guard = torch.full((need + 4096,), 0x5A, dtype=torch.uint8, device="cuda")
-    m = ffa.build_meta(sl, 16384, 16384, 128, out=guard[:fixed + 256])
+    m = ffa.build_meta(sl, 16384, 16384, 128, out=guard[:fixed + 256], validate=False)
     assert m.status() & ffa.META_ERR_CAPACITY
     assert bool((guard[fixed + 256:] == 0x5A).all())
 

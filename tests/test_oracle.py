@@ -180,12 +180,30 @@ def _random_table(rng, Tq, Tk, n):
     return out
 
 
+def _banded_table(rng, Tq, Tk):
+    """Disjoint table with several slices per query row: query bands, each with
+    2-4 disjoint key ranges of random types (the workload generator's recipe,
+    restated here so that the oracle pins do not depend on it)."""
+    cuts = sorted(rng.sample(range(1, Tq), 2))
+    b = [0] + cuts + [Tq]
+    out = []
+    for q0, q1 in zip(b[:-1], b[1:]):
+        n = rng.randint(2, 4)
+        pts = sorted(rng.sample(range(0, Tk + 1), 2 * n))
+        for i in range(n):
+            a, z = rng.randint(q0, q1 - 1), rng.randint(q0 + 1, q1)
+            qa, qz = min(a, z - 1), max(a + 1, z)
+            out.append((qa, qz, pts[2 * i], pts[2 * i + 1], rng.choice(TYPES)))
+    return out
+
+
 def test_random_tables_equal_sdpa_with_materialised_mask():
     rng = random.Random(3)
     for trial in range(12):
         Tq, Tk, H, Hkv = rng.randint(8, 60), rng.randint(8, 60), 4, rng.choice([1, 2, 4])
-        sl = _random_table(rng, Tq, Tk, rng.randint(1, 5))
+        sl = _random_table(rng, Tq, Tk, rng.randint(1, 5)) if trial % 2 else _banded_table(rng, Tq, Tk)
         q, k, v = _rand((Tq, H, 8), 100 + trial), _rand((Tk, Hkv, 8), 200 + trial), _rand((Tk, Hkv, 8), 300 + trial)
+        assert orc.validate(sl, Tq, Tk) == 0
         o, lse = orc.forward(q, k, v, sl)
         mask = torch.from_numpy(orc.dense_mask(sl, Tq, Tk).astype(bool))
         rep = H // Hkv
@@ -283,6 +301,54 @@ def test_backward_finite_differences(t):
             args_p[which], args_m[which] = xp, xm
             num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
         assert np.linalg.norm(num - g) <= 1e-6 * max(1.0, np.linalg.norm(g)), which
+
+
+def _autograd_dkdv(q, k, v, do, sl):
+    """dK, dV through torch SDPA (float64) with a materialised mask."""
+    Tq, H = q.shape[0], q.shape[1]
+    Tk, Hkv = k.shape[0], k.shape[1]
+    mask = torch.from_numpy(orc.dense_mask(sl, Tq, Tk).astype(bool))
+    empty = ~mask.any(dim=1)
+    mask_f = mask.clone()
+    mask_f[empty] = True
+    kk, vv = k.clone().requires_grad_(True), v.clone().requires_grad_(True)
+    rep = H // Hkv
+    o = _sdpa(q, kk.repeat_interleave(rep, 1), vv.repeat_interleave(rep, 1), mask=mask_f)
+    o = o * (~empty).to(o.dtype)[:, None, None]
+    (o * do).sum().backward()
+    return kk.grad.numpy(), vv.grad.numpy()
+
+
+def test_backward_keys_equals_autograd_on_sampled_keys():
+    """dK, dV restricted to sampled key rows and a subset of kv heads equal
+    the autograd gradient at those rows (several slices per query row, GQA,
+    rows without keys, a tiny batch budget so rows and windows are split)."""
+    rng = random.Random(21)
+    for trial in range(6):
+        Tq, Tk, Hkv = rng.randint(20, 70), rng.randint(20, 70), rng.choice([1, 2, 3])
+        H = Hkv * rng.choice([1, 2])
+        sl = _banded_table(rng, Tq, Tk)
+        q, k, v, do = (_rand(s, 500 + 10 * trial + n) for n, s in enumerate(
+            [(Tq, H, 8), (Tk, Hkv, 8), (Tk, Hkv, 8), (Tq, H, 8)]))
+        dk_ref, dv_ref = _autograd_dkdv(q, k, v, do, sl)
+        keys = np.array(rng.sample(range(Tk), rng.randint(1, Tk)))      # unsorted, distinct
+        heads = sorted(rng.sample(range(Hkv), rng.randint(1, Hkv)))
+        dK, dV = orc.backward_keys(q, k, v, do, sl, keys, kv_heads=heads,
+                                   max_elems=rng.choice([1 << 25, 97]))
+        np.testing.assert_allclose(dK, dk_ref[keys][:, heads], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(dV, dv_ref[keys][:, heads], rtol=1e-10, atol=1e-12)
+
+
+def test_backward_keys_scale_and_key_order():
+    """A non-default scale, repeated and unsorted keys: each output row is
+    the gradient of its own key."""
+    sl = [(0, 30, 0, 40, orc.CAUSAL), (0, 30, 40, 55, orc.BI_CAUSAL), (30, 50, 10, 55, orc.FULL)]
+    q, k, v, do = _rand((50, 2, 8), 1), _rand((55, 1, 8), 2), _rand((55, 1, 8), 3), _rand((50, 2, 8), 4)
+    dq, dk, dv = orc.backward(q, k, v, do, sl, scale=0.3)
+    keys = np.array([54, 3, 3, 40, 0, 39])
+    dK, dV = orc.backward_keys(q, k, v, do, sl, keys, scale=0.3)
+    np.testing.assert_allclose(dK, dk[keys], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dV, dv[keys], rtol=1e-12, atol=1e-13)
 
 
 def test_dk_sums_to_zero_and_dq_rows():

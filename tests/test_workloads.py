@@ -71,3 +71,17 @@ def test_tensor_generation_is_seeded():
     for k in t1:
         assert t1[k].dtype.is_floating_point and (t1[k] == t2[k]).all()
     assert not (wl.make_tensors(c, 2)["q"] == t1["q"]).all()
+
+
+def test_banded_tables_put_several_slices_on_one_row():
+    """The banded generator gives valid, disjoint tables in which some query
+    rows are covered by two or more slices."""
+    for seed in range(20):
+        rng = random.Random(seed)
+        Tq, Tk = rng.randint(50, 900), rng.randint(50, 900)
+        sl = wl.random_banded_slices(rng, Tq, Tk)
+        assert orc.validate(sl, Tq, Tk) == 0
+        cover = np.zeros(Tq, dtype=int)
+        for q0, q1, k0, k1, t in sl:
+            cover[q0:q1] += 1
+        assert cover.max() >= 2
