@@ -29,11 +29,12 @@ EXPORTED = (
     "ffa_block_meta_workspace_size", "ffa_build_block_meta", "ffa_block_meta_view", "ffa_fwd",
     "ffa_bwd_workspace_size", "ffa_bwd", "ffa_bwd_phases", "ffa_status_string", "ffa_abi_version",
     "ffa_fwd_ex", "ffa_bwd_ex", "ffa_chunk_areas", "ffa_dispatch_chunks", "ffa_rank_slices",
-    "ffa_fwd_grouped", "ffa_bwd_grouped",
+    "ffa_fwd_grouped", "ffa_bwd_grouped", "ffa_bwd_static_scratch",
 )
 MAX_MASK_GROUPS = 8             # FFA_MAX_MASK_GROUPS
 BWD_PRE, BWD_DKDV, BWD_DQ, BWD_ALL = 1, 2, 4, 7
 ACCUMULATE = 1                  # FFA_ACCUMULATE flag of ffa_fwd_ex / ffa_bwd_ex
+STATIC_SCRATCH_BYTES = 64 << 20 # FFA_STATIC_SCRATCH_BYTES of ffa_bwd_static_scratch
 
 
 class FFAError(RuntimeError):
@@ -104,6 +105,8 @@ def lib() -> ctypes.CDLL:
                                   TensorIn, i32, vp, vp, TensorOut, TensorOut, TensorOut, vp, sz, i32,
                                   ctypes.c_uint32, vp]
     L.ffa_bwd_grouped.restype = st
+    L.ffa_bwd_static_scratch.argtypes = L.ffa_bwd.argtypes[:-3] + [vp]
+    L.ffa_bwd_static_scratch.restype = st
     P32, P64 = ctypes.POINTER(i32), ctypes.POINTER(i64)
     L.ffa_chunk_areas.argtypes = [vp, i32, i32, i32, i32, vp]
     L.ffa_chunk_areas.restype = st
@@ -472,6 +475,23 @@ def bwd(q, k, v, o, lse, do, meta: BlockMeta, scale: float = None, dq=None, dk=N
     return dq, dk, dv
 
 
+def bwd_static_scratch(q, k, v, o, lse, do, meta: BlockMeta, scale: float = None, dq=None, dk=None,
+                       dv=None, stream=None):
+    """Backward with the library's static scratch array instead of a workspace
+    (ffa_bwd_static_scratch): for callers that cannot allocate device memory,
+    who pass dq, dk, dv.  Same results as ``bwd``; calls that may overlap on one
+    GPU must be serialised."""
+    _check_inputs(q, k, v, ((o, "o"), (do, "do")))
+    _check_lse(lse, q)
+    _check_meta(meta, q, k)
+    sh = _shape(q, k, scale)
+    dq, dk, dv = _grad_buffers(q, k, v, dq, dk, dv)
+    _check(lib().ffa_bwd_static_scratch(ctypes.byref(sh), _tin(q), _tin(k), _tin(v), _tin(o),
+                                        lse.data_ptr(), _tin(do), meta.ptr, _tout(dq), _tout(dk),
+                                        _tout(dv), _stream(stream)), "ffa_bwd_static_scratch")
+    return dq, dk, dv
+
+
 class FFAFunction(torch.autograd.Function):
     """Autograd wrapper: ``meta`` is one BlockMeta, or a list of them with
     ``kv_head_end`` for several masks in one launch."""
@@ -503,6 +523,7 @@ def ffa_attention(q, k, v, meta, scale: float = None, kv_head_end=None) -> torch
 
 
 __all__ = ["BWD_PRE", "BWD_DKDV", "BWD_DQ", "BWD_ALL", "ACCUMULATE", "build_meta", "fwd", "bwd", "ffa_attention", "FFAFunction", "BlockMeta", "lib",
+           "bwd_static_scratch", "STATIC_SCRATCH_BYTES",
            "meta_workspace_size", "bwd_workspace_size", "chunk_areas", "dispatch_chunks",
            "fwd_grouped", "bwd_grouped", "MAX_MASK_GROUPS",
            "rank_slices", "FFAError", "FULL", "CAUSAL", "INV_CAUSAL",

@@ -1,9 +1,11 @@
 // ffa_api.hip - host side of the libffa C ABI: argument validation, metadata
-// layout and kernel dispatch.  Nothing here allocates, synchronises or keeps
-// state; every call only enqueues kernels on the caller's stream.
+// layout and kernel dispatch.  Nothing here allocates or synchronises; every
+// call only enqueues kernels on the caller's stream.  The one piece of state
+// is the per-device address of the static backward scratch (end of file).
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "ffa_internal.hpp"
 
@@ -125,6 +127,7 @@ FFA_API const char* ffa_status_string(ffa_status s) {
     case FFA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case FFA_ERR_HIP: return "HIP launch failed";
     case FFA_ERR_BAD_SLICES: return "bad slice table";
+    case FFA_ERR_TOO_LARGE: return "shape needs more scratch than the static array holds";
   }
   return "unknown status";
 }
@@ -363,3 +366,55 @@ FFA_API ffa_status ffa_bwd_grouped(const ffa_shape* shape, ffa_tensor_in q, ffa_
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Backward for callers that cannot allocate: its scratch lives in a static
+// device array of FFA_STATIC_SCRATCH_BYTES.  Each GPU holds its own copy of
+// the array at its own address; host code never passes the symbol itself to
+// a kernel (in host code it names a host-side stand-in), only the address
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device and kept.
+// ---------------------------------------------------------------------------
+__device__ __attribute__((aligned(256))) char scratch[FFA_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+// Address of the scratch array on the current device (set up on first use).
+ffa_status static_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return FFA_ERR_HIP;
+  if (dev < 0 || dev >= MAX_DEVICES) return FFA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FFA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FFA_OK;
+}
+
+}  // namespace
+
+extern "C" FFA_API ffa_status ffa_bwd_static_scratch(const ffa_shape* shape, ffa_tensor_in q,
+                                                     ffa_tensor_in k, ffa_tensor_in v,
+                                                     ffa_tensor_in o, const float* lse,
+                                                     ffa_tensor_in dout, const void* d_meta,
+                                                     ffa_tensor_out dq, ffa_tensor_out dk,
+                                                     ffa_tensor_out dv, void* stream) {
+  size_t need = 0;
+  const ffa_status st = ffa_bwd_workspace_size(shape, &need);
+  if (st != FFA_OK) return st;
+  if (need > (size_t)FFA_STATIC_SCRATCH_BYTES) return FFA_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  const ffa_status sp = static_scratch(&ws);
+  if (sp != FFA_OK) return sp;
+  // the split counters are zeroed by the first backward kernel of the call
+  // (the dQ kernel with the row statistics), as with a caller's workspace
+  return ffa_bwd_phases(shape, q, k, v, o, lse, dout, d_meta, dq, dk, dv, ws,
+                        (size_t)FFA_STATIC_SCRATCH_BYTES, FFA_BWD_ALL, stream);
+}

@@ -28,9 +28,10 @@
  *  - lse is fp32 [num_heads_q][seqlen_q], natural log, including the softmax
  *    scale: lse_i = ln sum_{j valid} exp(scale * q_i . k_j).
  *  - Ownership: the caller allocates and frees every buffer.  The library
- *    allocates nothing, keeps no global mutable state, never synchronises, and
- *    only enqueues work on the given stream (a hipStream_t passed as void*;
- *    NULL is the default stream).
+ *    allocates nothing, never synchronises, and only enqueues work on the
+ *    given stream (a hipStream_t passed as void*; NULL is the default
+ *    stream).  Its only global state is the per-device address of the static
+ *    scratch array of ffa_bwd_static_scratch, looked up once per device.
  *  - Errors: problems visible on the host (null or misaligned pointers, bad
  *    shapes or strides, unsupported head_dim, a buffer that is too small) make
  *    the call return a non-zero ffa_status before anything is enqueued.  A
@@ -53,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FFA_ABI_VERSION 4
+#define FFA_ABI_VERSION 5
 
 #if defined(__GNUC__)
 #define FFA_API __attribute__((visibility("default")))
@@ -74,7 +75,8 @@ typedef enum {
   FFA_ERR_UNSUPPORTED = 2,         /* e.g. head_dim not 64 or 128 */
   FFA_ERR_WORKSPACE_TOO_SMALL = 3, /* meta_bytes or ws_bytes below the required size */
   FFA_ERR_HIP = 4,                 /* a kernel launch failed */
-  FFA_ERR_BAD_SLICES = 5           /* host slice table: range out of bounds or unknown type */
+  FFA_ERR_BAD_SLICES = 5,          /* host slice table: range out of bounds or unknown type */
+  FFA_ERR_TOO_LARGE = 6            /* the shape needs more scratch than the static array holds */
 } ffa_status;
 
 /* Flags of the device status word inside the block metadata. */
@@ -365,6 +367,30 @@ FFA_API ffa_status ffa_rank_slices(const int32_t* host_slices, int32_t num_slice
                                    const int32_t* chunks, int32_t num_chunks,
                                    int32_t* local_slices, int32_t max_local, int32_t* num_local,
                                    int32_t* kv_ranges, int32_t max_kv, int32_t* num_kv);
+
+/* ---------------------------------------------------------------------------
+ * Backward without a workspace argument.
+ *
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): ffa_bwd
+ * with its scratch (the -D / LSE rows, split counters and split partials of
+ * ffa_bwd_workspace_size) in a static device array of the library,
+ * FFA_STATIC_SCRATCH_BYTES per GPU, which every GPU the library runs on holds
+ * until the process ends.  The array's address on the current device is
+ * looked up on the first call there.  Results are those of ffa_bwd (same
+ * kernels, bitwise).  A shape whose ffa_bwd_workspace_size exceeds
+ * FFA_STATIC_SCRATCH_BYTES gives FFA_ERR_TOO_LARGE before anything is
+ * enqueued.  Every call on one GPU uses that GPU's one array: calls that may
+ * overlap on one GPU (other streams, other host threads) race and must be
+ * serialised by the caller.  No device memory is allocated or freed.
+ * ------------------------------------------------------------------------- */
+#define FFA_STATIC_SCRATCH_BYTES (64u << 20)
+
+FFA_API ffa_status ffa_bwd_static_scratch(const ffa_shape* shape, ffa_tensor_in q,
+                                          ffa_tensor_in k, ffa_tensor_in v, ffa_tensor_in o,
+                                          const float* lse, ffa_tensor_in dout, const void* d_meta,
+                                          ffa_tensor_out dq, ffa_tensor_out dk, ffa_tensor_out dv,
+                                          void* stream);
 
 /* Static description of a status code. */
 FFA_API const char* ffa_status_string(ffa_status status);

@@ -23,7 +23,7 @@ def declared_symbols():
 
 def test_exports_every_declared_symbol():
     names = declared_symbols()
-    assert len(names) == 16 and set(names) == set(ffa.EXPORTED)
+    assert len(names) == 17 and set(names) == set(ffa.EXPORTED)
     L = ffa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -35,8 +35,8 @@ def test_exports_every_declared_symbol():
 
 def test_abi_version_and_strings():
     L = ffa.lib()
-    assert L.ffa_abi_version() == 4
-    for code in range(6):
+    assert L.ffa_abi_version() == 5
+    for code in range(7):
         assert len(L.ffa_status_string(code)) > 0
     assert L.ffa_status_string(99) == b"unknown status"
 
@@ -135,6 +135,17 @@ def test_host_validation_returns_before_enqueue():
                              goodo, goodo, 0x100000, wsg.value, 7, 0, None) == 1
     assert L.ffa_bwd_grouped(P(sh), good, good, good, good, lse, good, 2, ok_m, ok_e, goodo,
                              goodo, goodo, 0x100000, wsg.value - 1, 7, 0, None) == 3
+    # the static-scratch backward: a shape whose workspace exceeds the static
+    # array is refused before the library touches the device
+    big = _shape(Tq=1 << 22, Tk=1 << 20, Hq=8, Hkv=8, d=128)     # 2 x 128 MiB of row statistics
+    need = ctypes.c_size_t()
+    assert L.ffa_bwd_workspace_size(P(big), P(need)) == 0 and need.value > ffa.STATIC_SCRATCH_BYTES
+    assert L.ffa_bwd_static_scratch(P(big), good, good, good, good, lse, good, meta, goodo, goodo, goodo,
+                                    None) == 6
+    assert L.ffa_bwd_static_scratch(P(_shape(d=96)), good, good, good, good, lse, good, meta, goodo,
+                                    goodo, goodo, None) == 2
+    assert L.ffa_bwd_static_scratch(None, good, good, good, good, lse, good, meta, goodo, goodo, goodo,
+                                    None) == 1
     # metadata build: bad sizes, misaligned buffer, too-small buffer
     n = ctypes.c_size_t()
     assert L.ffa_block_meta_workspace_size(-1, 10, 10, 64, None, P(n)) == 1
