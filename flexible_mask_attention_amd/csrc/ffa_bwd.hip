@@ -69,11 +69,63 @@ __global__ __launch_bounds__(NT) void ffa_bwd_pre_kernel(BwdArgs a) {
 constexpr int DQ_SK = 32;                       // keys per stage
 
 template <int D>
-constexpr int dq_nql() { return D == 128 ? 4 : 0; }
+constexpr int dq_nql() { return D == 128 ? 5 : 0; }
 
 template <int D>
 constexpr size_t dq_lds_bytes() {
   return 2 * 2 * DQ_SK * D * 2 + (size_t)(NT / 64) * dq_nql<D>() * 1024;
+}
+
+// S^T = K Q^T and dP^T = V dO^T of one 32-key stage at head_dim 128 (the
+// first three 16-wide d steps of Q in registers, the last five parked in LDS),
+// as one block with a ring of three 128-bit operand buffers: each MFMA's LDS
+// operand is read two to three reads ahead of its use instead of just before
+// it (the compiler's own schedule, register-bound at three waves per SIMD).  Same MFMAs in the same
+// order as the plain loop (bitwise identical sums).  The buffers and
+// accumulators are outputs, so the compiler keeps nothing else in them; the
+// block waits for its own LDS reads (a wait for at most N outstanding also
+// covers any older LDS or scalar loads) and ends with 16 wait states, more
+// than an 8-pass MFMA result needs before a VALU instruction may read it.
+#define FFA_RD(buf, addr, off) "ds_read_b128 " buf ", " addr " offset:" #off "\n\t"
+#define FFA_MF(d, a, b, c) "v_mfma_f32_32x32x16_bf16 " d ", " a ", " b ", " c "\n\t"
+#define FFA_WT(n) "s_waitcnt lgkmcnt(" #n ")\n\t"
+// operands: %0 S, %1 dP, %2-%4 buffers, %5-%7 Q chunks 0-2, %8-%15 dO chunks
+// 0-7, %16 / %17 K/V read address of column pair 0 / 1, %18 parked Q chunks 3-7
+#define FFA_SDP_BLOCK(K0, K1, K2, K3, V0, V1, V2, V3) \
+  FFA_RD("%2", "%16", K0) FFA_RD("%3", "%16", V0) FFA_RD("%4", "%17", K0) \
+  FFA_WT(2) FFA_MF("%0", "%2", "%5", "0") FFA_RD("%2", "%17", V0) \
+  FFA_WT(2) FFA_MF("%1", "%3", "%8", "0") FFA_RD("%3", "%16", K1) \
+  FFA_WT(2) FFA_MF("%0", "%4", "%6", "%0") FFA_RD("%4", "%16", V1) \
+  FFA_WT(2) FFA_MF("%1", "%2", "%9", "%1") FFA_RD("%2", "%17", K1) \
+  FFA_WT(2) FFA_MF("%0", "%3", "%7", "%0") FFA_RD("%3", "%18", 0) \
+  FFA_WT(2) FFA_MF("%1", "%4", "%10", "%1") FFA_RD("%4", "%17", V1) \
+  FFA_WT(1) FFA_MF("%0", "%2", "%3", "%0") FFA_RD("%2", "%16", K2) FFA_RD("%3", "%18", 1024) \
+  FFA_WT(2) FFA_MF("%1", "%4", "%11", "%1") FFA_RD("%4", "%16", V2) \
+  FFA_WT(1) FFA_MF("%0", "%2", "%3", "%0") FFA_RD("%2", "%17", K2) FFA_RD("%3", "%18", 2048) \
+  FFA_WT(2) FFA_MF("%1", "%4", "%12", "%1") FFA_RD("%4", "%17", V2) \
+  FFA_WT(1) FFA_MF("%0", "%2", "%3", "%0") FFA_RD("%2", "%16", K3) FFA_RD("%3", "%18", 3072) \
+  FFA_WT(2) FFA_MF("%1", "%4", "%13", "%1") FFA_RD("%4", "%16", V3) \
+  FFA_WT(1) FFA_MF("%0", "%2", "%3", "%0") FFA_RD("%2", "%17", K3) FFA_RD("%3", "%18", 4096) \
+  FFA_WT(2) FFA_MF("%1", "%4", "%14", "%1") FFA_RD("%4", "%17", V3) \
+  FFA_WT(1) FFA_MF("%0", "%2", "%3", "%0") \
+  FFA_WT(0) FFA_MF("%1", "%4", "%15", "%1") \
+  "s_nop 7\n\ts_nop 7"
+
+template <int STAGE>
+__device__ __forceinline__ void sdp_d128(f32x16& sacc, f32x16& pacc, const bf16x8 (&q)[8],
+                                         const bf16x8 (&g)[8], uint32_t k0, uint32_t k1,
+                                         uint32_t qp) {
+  u32x4 b0, b1, b2;
+#define FFA_SDP_OPS                                                                         \
+  : "=&v"(sacc), "=&v"(pacc), "=&v"(b0), "=&v"(b1), "=&v"(b2)                              \
+  : "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(g[0]), "v"(g[1]), "v"(g[2]), "v"(g[3]), \
+    "v"(g[4]), "v"(g[5]), "v"(g[6]), "v"(g[7]), "v"(k0), "v"(k1), "v"(qp)                 \
+  : "memory"
+  if constexpr (STAGE == 0)
+    asm volatile(FFA_SDP_BLOCK(0, 2048, 4096, 6144, 8192, 10240, 12288, 14336) FFA_SDP_OPS);
+  else
+    asm volatile(FFA_SDP_BLOCK(16384, 18432, 20480, 22528, 24576, 26624, 28672, 30720) FFA_SDP_OPS);
+#undef FFA_SDP_OPS
 }
 
 // PRE: also compute this block's -D and LSE log2 e rows (the bwd_pre work)
@@ -179,6 +231,11 @@ __global__ __launch_bounds__(NT, 3) __attribute__((amdgpu_waves_per_eu(3, 3))) v
   int raddr[2], taddr[2];
 #pragma unroll
   for (int p = 0; p < 2; ++p) raddr[p] = lds_pos(l32, 2 * p + h32);
+  // LDS byte addresses of this lane's 128-bit K / V operand reads (column
+  // pair 0 and 1) and of its parked Q chunks, for the S / dP block below
+  const uint32_t smem_base = (uint32_t)(size_t)((__attribute__((address_space(3))) char*)smem);
+  const uint32_t kbase0 = smem_base + raddr[0], kbase1 = smem_base + raddr[1];
+  const uint32_t qbase = (uint32_t)(size_t)((__attribute__((address_space(3))) char*)qlds);
 #pragma unroll
   for (int j = 0; j < 2; ++j)
     taddr[j] = lds_pos(4 * h32 + (t16 >> 2) + 8 * j, 2 * (g16 & 1) + ((t16 >> 1) & 1)) + 8 * (t16 & 1);
@@ -231,23 +288,29 @@ __global__ __launch_bounds__(NT, 3) __attribute__((amdgpu_waves_per_eu(3, 3))) v
 
     if (live) {
       // S^T = K Q^T and dP^T = V dO^T; lane = query row, registers = keys 8(r/4) + 4*h32 + r%4
-      f32x16 sacc = f32x16{}, pacc = f32x16{};
+      f32x16 sacc, pacc;
+      if constexpr (D == 128 && NQL == 5) {
+        sdp_d128<stage>(sacc, pacc, qop, gop, kbase0, kbase1, qbase);
+      } else {
+        sacc = f32x16{};
+        pacc = f32x16{};
 #pragma unroll
-      for (int k = 0; k < KS; ++k) {
-        bf16x8 ka, va, qv;
-        u32x4 u1 = *(const __attribute__((address_space(3))) u32x4*)(lb + (k >> 1) * GB + raddr[k & 1]);
-        u32x4 u2 = *(const __attribute__((address_space(3))) u32x4*)(lb + TILE_B + (k >> 1) * GB + raddr[k & 1]);
-        __builtin_memcpy(&ka, &u1, 16);
-        __builtin_memcpy(&va, &u2, 16);
-        if (k < QREG) {
-          qv = qop[k];
-        } else {
-          u32x4 uq = *(const __attribute__((address_space(3))) u32x4*)(
-              (const __attribute__((address_space(3))) char*)qlds + (k - QREG) * 1024);
-          __builtin_memcpy(&qv, &uq, 16);
+        for (int k = 0; k < KS; ++k) {
+          bf16x8 ka, va, qv;
+          u32x4 u1 = *(const __attribute__((address_space(3))) u32x4*)(lb + (k >> 1) * GB + raddr[k & 1]);
+          u32x4 u2 = *(const __attribute__((address_space(3))) u32x4*)(lb + TILE_B + (k >> 1) * GB + raddr[k & 1]);
+          __builtin_memcpy(&ka, &u1, 16);
+          __builtin_memcpy(&va, &u2, 16);
+          if (k < QREG) {
+            qv = qop[k];
+          } else {
+            u32x4 uq = *(const __attribute__((address_space(3))) u32x4*)(
+                (const __attribute__((address_space(3))) char*)qlds + (k - QREG) * 1024);
+            __builtin_memcpy(&qv, &uq, 16);
+          }
+          sacc = mfma32(ka, qv, sacc);
+          pacc = mfma32(va, gop[k], pacc);
         }
-        sacc = mfma32(ka, qv, sacc);
-        pacc = mfma32(va, gop[k], pacc);
       }
       if (masked) {
 #pragma unroll

@@ -12,12 +12,15 @@
 // lane owns one query row: its softmax statistics stay in registers and only
 // one half-wave swap is needed per row max.  The P^T accumulator registers
 // feed the next MFMA (O^T += V^T P^T) directly as its B operand; V^T comes
-// from LDS through ds_read_b64_tr_b16.  Each 64-key tile of the lists is
-// streamed as two 32-key stages through a double-buffered LDS ring (32 KB per
-// workgroup at d = 128); the loads for stage s+1 are issued before stage s is
-// computed.  At under 170 VGPRs and 32 KB of LDS, three workgroups share a
-// CU, i.e. three waves per SIMD hide each other's LDS, exponent and MFMA
-// latencies (measured faster than two waves of two 32-row blocks each, which
+// from LDS through ds_read_b64_tr_b16.  Each 64-key tile of the lists (Full
+// tiles first, then the Partial ones) is streamed as two 32-key stages through
+// a double-buffered LDS ring (32 KB per workgroup at d = 128); the loads for
+// stage s+1 are issued before stage s is computed.  Once every row of a wave
+// has a running max, a stage forms P against it without computing the
+// stage's row max, and only a partial row sum past 2^8 sends the stage back
+// to the exact path (row max, rescale, P again).  At under 170 VGPRs and
+// 32 KB of LDS, three workgroups share a CU, i.e. three waves per SIMD hide
+// each other's LDS, exponent and MFMA latencies (measured faster than two waves of two 32-row blocks each, which
 // halve the LDS reads per MFMA but need 253 VGPRs).
 #include <type_traits>
 
@@ -94,7 +97,9 @@ void ffa_fwd_kernel(FwdArgs a) {
   dm.init(wid & 1, lane, wid < 2 ? a.k_ts : a.v_ts);
   const __bf16* kbase = a.k + (int64_t)kvh * a.k_hs;
   const __bf16* vbase = a.v + (int64_t)kvh * a.v_hs;
-  auto tile_of = [&](int t) { return t < nP ? pidx[t] : fidx[t - nP]; };
+  // Full tiles first: the running max then starts from a whole 32-key stage
+  // for every row before the diagonal (Partial) tiles
+  auto tile_of = [&](int t) { return t < nF ? fidx[t] : pidx[t - nF]; };
   auto issue = [&](int u, int stage) {
     const int key0 = tile_of(u / HALVES) * BN_F + (u % HALVES) * SK;
     char* st = smem + stage * STAGE_B;
@@ -107,12 +112,22 @@ void ffa_fwd_kernel(FwdArgs a) {
   for (int i = 0; i < MB; ++i) oacc[i] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;   // running max of raw scores, partial row sum
   const float c = a.scale_log2;           // > 0
-  const float thr = 8.f / c;              // rescale only when the max grows by 2^8
+  // m_run * c, or 0 while the row has seen no valid key
+  float mc = 0.f;
+  // Every row of the wave has a finite running max.  Until then each live
+  // stage takes the exact path; afterwards a stage first forms P against the
+  // stored max and falls back to the exact path only when some lane's partial
+  // row sum exceeds 2^8, i.e. when a score may have grown past the stored max
+  // by more than 8 in the exp2 domain (P <= row sum, so below that bound every
+  // P is at most 2^8, the same bound the exact path's lazy rescale keeps).
+  bool all_finite = false;
+  constexpr float PSUM_LIMIT = 256.f;
+  const float thr = 8.f / c;              // exact path: rescale only when the max grows by 2^8
 
   auto stage_fn = [&](auto stage_c, int u) {
     constexpr int stage = decltype(stage_c)::value;
     const int t = u / HALVES;
-    const bool masked = t < nP;
+    const bool masked = t >= nF;
     const int key0 = tile_of(t) * BN_F + (u % HALVES) * SK;
     if (u + 1 < nU) issue(u + 1, stage ^ 1);
     const __attribute__((address_space(3))) char* lb =
@@ -152,29 +167,45 @@ void ffa_fwd_kernel(FwdArgs a) {
         for (int r = 0; r < 16; ++r)
           if (!((w >> (8 * (r >> 2) + (r & 3))) & 1u)) sacc[r] = -INFINITY;
       }
-
-      float mx = sacc[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
-      mx = wave_swap_max(mx);
-      if (__ballot(mx > m_run + thr) != 0) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
-        l_run *= alpha;
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[mb][r] *= alpha;
-        m_run = m_new;
-      }
-      const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
       bf16x8 pop[2];
       float psum = 0.f;
+      bool exact = !all_finite;
+      if (!exact) {
+        // P against the stored max; the scores stay in sacc for the exact path
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -mc));
-        pop[r >> 3][r & 7] = static_cast<__bf16>(pv);
-        psum += pv;
+        for (int r = 0; r < 16; ++r) {
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -mc));
+          pop[r >> 3][r & 7] = static_cast<__bf16>(pv);
+          psum += pv;
+        }
+        exact = __ballot(!(psum <= PSUM_LIMIT)) != 0;
+      }
+      if (exact) {
+        // exact path: the row max of this stage, rescale O and l to it when it
+        // grew, P against the new max
+        float mx = sacc[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+        mx = wave_swap_max(mx);
+        if (__ballot(mx > m_run + thr) != 0) {
+          const float m_new = fmaxf(m_run, mx);
+          const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
+          l_run *= alpha;
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[mb][r] *= alpha;
+          m_run = m_new;
+        }
+        mc = (m_run == -INFINITY) ? 0.f : m_run * c;
+        all_finite = __ballot(m_run == -INFINITY) == 0;
+        psum = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -mc));
+          pop[r >> 3][r & 7] = static_cast<__bf16>(pv);
+          psum += pv;
+        }
       }
       l_run += psum;
 
