@@ -80,6 +80,37 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   cint32_t* fidx = mv.var + hd->list_off[L_KF] + f0;
   cint32_t* pidx = mv.var + hd->list_off[L_KM] + p0;
 
+  // Step u covers query head kvh*G + u % G of list entry nT - 1 - u / G: the
+  // lists (Partial, then Full, ascending) are walked backwards and the heads
+  // sharing this key head are interleaved, so every key block of a causal
+  // sequence starts at the sequence's last query tile and the blocks resident
+  // on one XCD move through the same Q / dO tiles at about the same time.
+  const int total = G * nT;
+  // this workgroup's steps: all of them, or one half of a split block
+  const int ubeg = part == 1 ? total / 2 : 0;
+  const int uend = part == 0 ? total / 2 : total;
+  auto tile_of = [&](int t) { return t < nP ? pidx[t] : fidx[t - nP]; };
+  TileDma<D, BM_B> dq_dma, dg_dma;
+  dq_dma.init(wid, lane, a.q_ts);
+  dg_dma.init(wid, lane, a.do_ts);
+  auto issue = [&](int u, int stage) {
+    const int hq = kvh * G + u % G;
+    const int m = tile_of(nT - 1 - u / G);
+    char* st = smem + stage * STAGE_B;
+    const int vr = a.Tq - m * BM_B;
+    dq_dma.load(a.q + (int64_t)hq * a.q_hs, a.q_ts, m * BM_B, vr, st);
+    dg_dma.load(a.dout + (int64_t)hq * a.do_hs, a.do_ts, m * BM_B, vr, st + TILE_B);
+    if (wid < 2) {
+      const float* src = (wid == 0 ? a.lvec : a.dvec) + (int64_t)hq * a.Tq + m * BM_B;
+      const int rows = vr < 0 ? 0 : (vr > BM_B ? BM_B : vr);
+      const i32x4 r = make_rsrc(src, (uint32_t)(rows * 4));
+      dma4(r, st + 2 * TILE_B + wid * BM_B * 4, lane * 4);
+    }
+  };
+  // the first tile's loads go out before the K / V loads, so that the two
+  // memory round trips of the prologue overlap
+  if (ubeg < uend) issue(ubeg, 0);
+
   // K and V as B operands: lane holds K[key][16k + 8*h32 + e]
   bf16x8 kop[KS], vop[KS];
   {
@@ -108,10 +139,6 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     taddr[j] = lds_pos(4 * h32 + (t16 >> 2) + 8 * j, 2 * (g16 & 1) + ((t16 >> 1) & 1)) + 8 * (t16 & 1);
   const int laddr = 2 * TILE_B + 16 * h32;   // row-stat reads: + (32qb + 8j) * 4
 
-  TileDma<D, BM_B> dq_dma, dg_dma;
-  dq_dma.init(wid, lane, a.q_ts);
-  dg_dma.init(wid, lane, a.do_ts);
-
   f32x16 dkacc[MB], dvacc[MB];
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
@@ -119,31 +146,9 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     dvacc[i] = f32x16{};
   }
 
-  // Step u covers query head kvh*G + u % G of list entry nT - 1 - u / G: the
-  // lists (Partial, then Full, ascending) are walked backwards and the heads
-  // sharing this key head are interleaved, so every key block of a causal
-  // sequence starts at the sequence's last query tile and the blocks resident
-  // on one XCD move through the same Q / dO tiles at about the same time.
-  const int total = G * nT;
-  // this workgroup's steps: all of them, or one half of a split block
-  const int ubeg = part == 1 ? total / 2 : 0;
-  const int uend = part == 0 ? total / 2 : total;
-  auto tile_of = [&](int t) { return t < nP ? pidx[t] : fidx[t - nP]; };
-  auto issue = [&](int u, int stage) {
-    const int hq = kvh * G + u % G;
-    const int m = tile_of(nT - 1 - u / G);
-    char* st = smem + stage * STAGE_B;
-    const int vr = a.Tq - m * BM_B;
-    dq_dma.load(a.q + (int64_t)hq * a.q_hs, a.q_ts, m * BM_B, vr, st);
-    dg_dma.load(a.dout + (int64_t)hq * a.do_hs, a.do_ts, m * BM_B, vr, st + TILE_B);
-    if (wid < 2) {
-      const float* src = (wid == 0 ? a.lvec : a.dvec) + (int64_t)hq * a.Tq + m * BM_B;
-      const int rows = vr < 0 ? 0 : (vr > BM_B ? BM_B : vr);
-      const i32x4 r = make_rsrc(src, (uint32_t)(rows * 4));
-      dma4(r, st + 2 * TILE_B + wid * BM_B * 4, lane * 4);
-    }
-  };
   const float c = a.scale_log2;
+  int mask_tile = -1;        // tile whose Partial mask mask_keep holds
+  uint64_t mask_keep = 0;
 
   auto tile = [&](auto stage_c, int u) {
     constexpr int stage = decltype(stage_c)::value;
@@ -159,20 +164,27 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     // with no valid pair for any of the wave's keys is skipped.
     uint64_t mk = 0, mkf = 0;
     if (masked) {
-      const int m0 = m * BM_B;
-      const int mf = m0 / BM_F;
-      const int s0 = mv.qs_off[mf], nS = mv.qs_off[mf + 1] - s0;
-      cint32_t* sidx = mv.var + hd->list_off[L_QS] + s0;
-      for (int si = 0; si < nS; ++si) {
-        const Slice sl = load_slice(mv.slices, sidx[si]);
-        int lo, hi;
-        col_interval(sl, key, lo, hi);
-        lo = max(lo, m0);
-        hi = min(hi, m0 + BM_B - 1);
-        if (lo <= hi) mk |= bit_range(lo - m0, hi - m0);
+      // the query heads of one tile come one after the other and share its
+      // mask: it is built at the first of them and kept for the rest
+      if (m != mask_tile) {
+        const int m0 = m * BM_B;
+        const int mf = m0 / BM_F;
+        const int s0 = mv.qs_off[mf], nS = mv.qs_off[mf + 1] - s0;
+        cint32_t* sidx = mv.var + hd->list_off[L_QS] + s0;
+        for (int si = 0; si < nS; ++si) {
+          const Slice sl = load_slice(mv.slices, sidx[si]);
+          int lo, hi;
+          col_interval(sl, key, lo, hi);
+          lo = max(lo, m0);
+          hi = min(hi, m0 + BM_B - 1);
+          if (lo <= hi) mkf |= bit_range(lo - m0, hi - m0);
+        }
+        mask_tile = m;
+        mask_keep = mkf;
+      } else {
+        mkf = mask_keep;
       }
-      mkf = mk;
-      mk >>= 4 * h32;
+      mk = mkf >> (4 * h32);
     }
 
     // one 32-row half at a time, so that only one S / dP pair is live
@@ -250,7 +262,6 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     __syncthreads();
   };
 
-  if (ubeg < uend) issue(ubeg, 0);
   wait_dma();
   __syncthreads();
   for (int u = ubeg; u < uend; u += 2) {

@@ -122,6 +122,21 @@ void ffa_fwd_kernel(FwdArgs a) {
   // P is at most 2^8, the same bound the exact path's lazy rescale keeps).
   bool all_finite = false;
   constexpr float PSUM_LIMIT = 256.f;
+
+  // The valid keys of a row inside one slice form one interval, and a row's
+  // valid keys are the union over the block's slices.  With at most NI slices
+  // on the block the intervals of this lane's row are found once, here, so a
+  // Partial stage builds its key mask from registers instead of reading the
+  // slice table again.
+  constexpr int NI = 4;
+  int ilo[NI], ihi[NI];
+  const bool iv_reg = nP > 0 && nS <= NI;
+#pragma unroll
+  for (int si = 0; si < NI; ++si) {
+    ilo[si] = 1;
+    ihi[si] = 0;
+    if (iv_reg && si < nS) row_interval(load_slice(mv.slices, sidx[si]), row0, ilo[si], ihi[si]);
+  }
   const float thr = 8.f / c;              // exact path: rescale only when the max grows by 2^8
 
   auto stage_fn = [&](auto stage_c, int u) {
@@ -139,17 +154,24 @@ void ffa_fwd_kernel(FwdArgs a) {
     uint32_t w = ~0u;
     bool live = true;
     if (masked) {
-      uint64_t mk = 0;
-      for (int si = 0; si < nS; ++si) {
-        const Slice sl = load_slice(mv.slices, sidx[si]);
-        int lo, hi;
-        row_interval(sl, row0, lo, hi);
-        lo = max(lo, key0);
-        hi = min(hi, key0 + SK - 1);
-        if (lo <= hi) mk |= bit_range(lo - key0, hi - key0);
+      uint32_t mk = 0;
+      if (iv_reg) {
+#pragma unroll
+        for (int si = 0; si < NI; ++si) {
+          const int lo = max(ilo[si], key0), hi = min(ihi[si], key0 + SK - 1);
+          if (lo <= hi) mk |= bit_range32(lo - key0, hi - key0);
+        }
+      } else {
+        for (int si = 0; si < nS; ++si) {
+          int lo, hi;
+          row_interval(load_slice(mv.slices, sidx[si]), row0, lo, hi);
+          lo = max(lo, key0);
+          hi = min(hi, key0 + SK - 1);
+          if (lo <= hi) mk |= bit_range32(lo - key0, hi - key0);
+        }
       }
       live = __ballot(mk != 0) != 0;
-      w = static_cast<uint32_t>(mk >> (4 * h32));   // register r holds key 8(r/4) + 4*h32 + r%4
+      w = mk >> (4 * h32);   // register r holds key 8(r/4) + 4*h32 + r%4
     }
 
     if (live) {

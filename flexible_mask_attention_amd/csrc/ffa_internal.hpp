@@ -178,6 +178,11 @@ __device__ __forceinline__ uint64_t bit_range(int a, int b) {
   return (~0ull >> (63 - (b - a))) << a;
 }
 
+// bits [a, b] of a 32-bit word (0 <= a <= b <= 31)
+__device__ __forceinline__ uint32_t bit_range32(int a, int b) {
+  return (~0u >> (31 - (b - a))) << a;
+}
+
 // ---------------------------------------------------------------------------
 // MFMA and register types.
 // ---------------------------------------------------------------------------
