@@ -20,6 +20,7 @@ import os
 import sys
 import time
 
+import numpy as np
 import torch
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -263,28 +264,54 @@ def host_threads():
     return n, aff
 
 
-def cpu_baseline(call, seed, area, min_seconds=10.0):
-    """The fp64 oracle, untuned, timed on the host cores: forward + backward of
-    the whole workload (all heads, full mask), repeated until at least
-    ``min_seconds`` have passed.  Inputs are the CPU-seeded tensors of the
-    same shapes."""
+def cpu_baseline(call, seed, area, min_seconds=10.0, full_limit_tflop=3.0):
+    """The fp64 oracle, untuned, timed on the host cores.  A workload whose
+    whole forward + backward is at most ``full_limit_tflop`` TFLOP (the 256-token
+    and 16K workloads) runs whole, all heads and the full mask, repeated until
+    ``min_seconds`` have passed.  A larger one runs on a bounded sample: O, LSE
+    and dQ (``forward_backward_rows``) of blocks of 256 consecutive query rows at
+    seeded random offsets, all query heads, until ``min_seconds`` have passed; its
+    FLOPs are the algorithmic ones of those rows (8 d per valid pair and head:
+    Q K^T, P V, dO V^T, dS K).  Inputs are the CPU-seeded tensors of the same
+    shapes."""
     from oracle import ffa_oracle as orc
     threads, aff = host_threads()
     torch.set_num_threads(threads)
     T = wl.make_tensors(call, seed)
+    full = 4.0 * call.d * area * call.Hq * 3.5
     reps, t0 = 0, time.perf_counter()
-    while True:
-        orc.forward(T["q"], T["k"], T["v"], call.slices)
-        orc.backward(T["q"], T["k"], T["v"], T["do"], call.slices)
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds or reps >= 5:
-            break
-    f = 4.0 * call.d * area * call.Hq * 3.5 * reps
-    return {"value": round(f / dt / 1e12, 4), "unit": "TFLOP/s", "cores": torch.get_num_threads(),
+    if full <= full_limit_tflop * 1e12:
+        while True:
+            orc.forward(T["q"], T["k"], T["v"], call.slices)
+            orc.backward(T["q"], T["k"], T["v"], T["do"], call.slices)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds or reps >= 5:
+                break
+        f = full * reps
+        sample = (f"whole workload (all {call.Hq} query heads, full mask), fwd + bwd, "
+                  f"{reps} pass(es) in {dt:.1f} s")
+    else:
+        g = torch.Generator().manual_seed(seed)
+        blocks = torch.randperm((call.Tq + 255) // 256, generator=g).tolist()
+        done, pairs = 0, 0
+        for b in blocks:
+            rows = np.arange(256 * b, min(256 * b + 256, call.Tq))
+            orc.forward_backward_rows(T["q"], T["k"], T["v"], T["do"], call.slices, rows)
+            for sl in call.slices:
+                lo, hi, ok = orc.row_intervals_vec(sl, rows)
+                pairs += int(np.where(ok, hi - lo + 1, 0).sum())
+            done += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds:
+                break
+        f = 8.0 * call.d * pairs * call.Hq
+        sample = (f"{done} block(s) of 256 consecutive query rows at seeded random offsets of {call.Tq}, "
+                  f"all {call.Hq} query heads: O, LSE and dQ of those rows (oracle "
+                  f"forward_backward_rows), {pairs} valid pairs per head, {dt:.1f} s")
+    return {"value": round(f / dt / 1e12, 4), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle", "affinity_cores": aff, "blas_threads": torch.get_num_threads(),
-            "sample": f"whole workload (all {call.Hq} query heads, full mask), fwd + bwd, "
-                      f"{reps} pass(es) in {dt:.1f} s"}
+            "seconds": round(dt, 2), "sample": sample}
 
 
 def main():
