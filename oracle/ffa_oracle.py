@@ -211,18 +211,23 @@ def validate(slices: Sequence, Tq: int, Tk: int) -> int:
             flags |= ERR_TYPE
             continue
         good.append(s)
-    # overlap: some row has intersecting intervals from two slices
+    # overlap: some row has intersecting intervals from two slices.  Two
+    # slices whose query ranges or key ranges do not intersect share no pair;
+    # that test is done for all later slices at once, and only the pairs
+    # passing it are compared row by row.
+    G = np.asarray(good, dtype=np.int64).reshape(-1, 5)
     for a in range(len(good)):
-        for b in range(a + 1, len(good)):
-            sa, sb = good[a], good[b]
-            r0, r1 = max(sa[0], sb[0]), min(sa[1], sb[1])
-            if r0 >= r1 or max(sa[2], sb[2]) >= min(sa[3], sb[3]):
-                continue
-            rows = np.arange(r0, r1)
+        sa = good[a]
+        rest = G[a + 1:]
+        cand = np.nonzero((np.maximum(rest[:, 0], sa[0]) < np.minimum(rest[:, 1], sa[1])) &
+                          (np.maximum(rest[:, 2], sa[2]) < np.minimum(rest[:, 3], sa[3])))[0]
+        for c in cand:
+            sb = good[a + 1 + int(c)]
+            rows = np.arange(max(sa[0], sb[0]), min(sa[1], sb[1]))
             la, ha, oka = row_intervals_vec(sa, rows)
             lb, hb, okb = row_intervals_vec(sb, rows)
             if np.any(oka & okb & (np.maximum(la, lb) <= np.minimum(ha, hb))):
-                flags |= ERR_OVERLAP
+                return flags | ERR_OVERLAP
     return flags
 
 

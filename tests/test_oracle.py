@@ -445,6 +445,26 @@ def test_validate_flags():
     assert orc.dense_mask(comp, 8, 8).max() == 1
 
 
+def test_validate_overlap_equals_dense_count():
+    """The overlap flag against its definition: two slices share a valid
+    (i, j) iff the materialised count of slices containing some cell exceeds
+    one.  Random small tables of every mask type, many of them overlapping,
+    with Lq != Lk and slices touching along the diagonal."""
+    rng = random.Random(31)
+    seen = [0, 0]
+    for _ in range(600):
+        T = rng.choice([6, 11, 24])
+        sl = []
+        for _ in range(rng.randint(2, 5)):
+            a, b = sorted(rng.sample(range(T + 1), 2))
+            c, d = sorted(rng.sample(range(T + 1), 2))
+            sl.append((a, b, c, d, rng.randint(0, 3)))
+        want = orc.ERR_OVERLAP if orc.dense_mask(sl, T, T).max() > 1 else 0
+        assert orc.validate(sl, T, T) == want, sl
+        seen[want != 0] += 1
+    assert min(seen) > 100
+
+
 # ------------------------------------------------- planted mistakes ----
 
 def test_pins_catch_planted_mistakes(monkeypatch):
