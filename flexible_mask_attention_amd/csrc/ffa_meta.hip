@@ -102,37 +102,87 @@ __global__ void meta_init_kernel(const int32_t* __restrict__ slices, void* meta,
     dst[i] = slices[i];
 }
 
-// Per-slice bounds / type checks and pairwise disjointness, one thread per
-// ordered pair (a <= b) of a 16 x 16 tile of pairs.  Two slices overlap iff
-// some shared row has intersecting key intervals.
-__device__ void validate_tile(void* meta, int tile) {
+// Per-slice bounds and type checks, one thread per slice.
+__device__ void check_slices(void* meta, int blk) {
   MetaPtrs p = meta_ptrs(meta);
   const int S = p.hdr->num_slices, Tq = p.hdr->seqlen_q, Tk = p.hdr->seqlen_k;
-  const int nt = (S + 15) / 16;
-  const int a = (tile / nt) * 16 + (threadIdx.x >> 4);
-  const int b = (tile % nt) * 16 + (threadIdx.x & 15);
-  if (a >= S || b >= S || b < a) return;
-  const Slice sa = load_slice(p.slices, a);
-  if (a == b) {
-    const bool bounds = 0 <= sa.q0 && sa.q0 <= sa.q1 && sa.q1 <= Tq && 0 <= sa.k0 &&
-                        sa.k0 <= sa.k1 && sa.k1 <= Tk;
-    int flags = 0;
-    if (!bounds) flags |= FFA_META_ERR_BOUNDS;
-    else if (sa.t < 0 || sa.t > 3) flags |= FFA_META_ERR_TYPE;
-    if (flags) atomicOr(&p.hdr->status, flags);
-    return;
+  const int a = blk * MT + threadIdx.x;
+  if (a >= S) return;
+  const Slice s = load_slice(p.slices, a);
+  const bool bounds = 0 <= s.q0 && s.q0 <= s.q1 && s.q1 <= Tq && 0 <= s.k0 && s.k0 <= s.k1 && s.k1 <= Tk;
+  int flags = 0;
+  if (!bounds) flags |= FFA_META_ERR_BOUNDS;
+  else if (s.t < 0 || s.t > 3) flags |= FFA_META_ERR_TYPE;
+  if (flags) atomicOr(&p.hdr->status, flags);
+}
+
+// A slice's valid keys in row i are [lo(i), hi(i)] with both ends linear in i
+// (slope 1 where the mask type bounds that side by the diagonal, else 0), on
+// the rows [A, B] where that interval is not empty (see row_interval: inside
+// the slice's rows the causal bound never exceeds Lk - 1).
+struct RowLines {
+  int64_t A, B, lc, hc;
+  int ls, hs;
+};
+
+__device__ RowLines row_lines(const Slice& s) {
+  const int64_t Lq = s.q1 - s.q0, Lk = s.k1 - s.k0, D = Lk - Lq;
+  const bool inv = (s.t == FFA_INV_CAUSAL) | (s.t == FFA_BI_CAUSAL);
+  const bool cau = (s.t == FFA_CAUSAL) | (s.t == FFA_BI_CAUSAL);
+  RowLines r;
+  r.A = s.q0;
+  r.B = static_cast<int64_t>(s.q1) - 1;
+  if (cau) r.A = max(r.A, static_cast<int64_t>(s.q0) - D);     // r + D >= 0
+  if (inv) r.B = min(r.B, static_cast<int64_t>(s.q0) + Lk - 1);  // r <= Lk - 1
+  if (Lk <= 0 || (inv && cau && D < 0)) r.B = r.A - 1;            // no valid pair
+  r.ls = inv ? 1 : 0;
+  r.lc = inv ? static_cast<int64_t>(s.k0) - s.q0 : s.k0;
+  r.hs = cau ? 1 : 0;
+  r.hc = cau ? static_cast<int64_t>(s.k0) - s.q0 + D : static_cast<int64_t>(s.k0) + Lk - 1;
+  return r;
+}
+
+// Do two slices share a valid (query, key) pair?  On their common valid rows
+// [R0, R1], g(i) = min(hi_a, hi_b) - max(lo_a, lo_b) is concave and piecewise
+// linear (a minimum of lines minus a maximum of lines), so its largest value
+// is taken at R0, R1 or a row where two lines of different slope cross; those
+// crossings are integers because the slopes differ by exactly 1.  The pair
+// overlaps iff g >= 0 at one of these at most four rows.
+__device__ bool pair_overlaps(const Slice& sa, const Slice& sb) {
+  const RowLines x = row_lines(sa), y = row_lines(sb);
+  const int64_t R0 = max(x.A, y.A), R1 = min(x.B, y.B);
+  if (R0 > R1) return false;
+  auto meets = [&](int64_t i) {
+    const int64_t hi = min(x.hc + x.hs * i, y.hc + y.hs * i);
+    const int64_t lo = max(x.lc + x.ls * i, y.lc + y.ls * i);
+    return hi >= lo;
+  };
+  if (meets(R0) || meets(R1)) return true;
+  if (x.hs != y.hs) {
+    const int64_t c = (y.hc - x.hc) / (x.hs - y.hs);
+    if (c > R0 && c < R1 && meets(c)) return true;
   }
-  const Slice sb = load_slice(p.slices, b);
-  if (!slice_ok(sa, Tq, Tk) || !slice_ok(sb, Tq, Tk)) return;
-  const int r0 = max(sa.q0, sb.q0), r1 = min(sa.q1, sb.q1);
-  if (r0 >= r1 || max(sa.k0, sb.k0) >= min(sa.k1, sb.k1)) return;
-  for (int i = r0; i < r1; ++i) {
-    int la, ha, lb, hb;
-    row_interval(sa, i, la, ha);
-    row_interval(sb, i, lb, hb);
-    if (la <= ha && lb <= hb && max(la, lb) <= min(ha, hb)) {
-      atomicOr(&p.hdr->status, FFA_META_ERR_OVERLAP);
-      return;
+  if (x.ls != y.ls) {
+    const int64_t c = (y.lc - x.lc) / (x.ls - y.ls);
+    if (c > R0 && c < R1 && meets(c)) return true;
+  }
+  return false;
+}
+
+// Disjointness, tested in the query block where two slices' common rows
+// begin: both are on that block's slice list, and every pair of slices with
+// common rows is tested by exactly one block.  The cost is the sum over query
+// blocks of (slices meeting the block)^2 / 2, so a table whose rows each meet
+// a bounded number of slices is checked in time linear in its size.
+__device__ void validate_pairs(MetaPtrs p, const int32_t* list, int k, int a0, int a1) {
+  for (int x = 0; x + 1 < k; ++x) {
+    const Slice sa = load_slice(p.slices, list[x]);
+    for (int y = x + 1 + static_cast<int>(threadIdx.x); y < k; y += MT) {
+      const Slice sb = load_slice(p.slices, list[y]);
+      const int first = max(sa.q0, sb.q0);
+      if (first < a0 || first >= a1 || first >= min(sa.q1, sb.q1)) continue;
+      if (max(sa.k0, sb.k0) >= min(sa.k1, sb.k1)) continue;
+      if (pair_overlaps(sa, sb)) atomicOr(&p.hdr->status, FFA_META_ERR_OVERLAP);
     }
   }
 }
@@ -240,6 +290,11 @@ __device__ void tiles_block(void* meta, int own, TilesLds& sm) {
   __syncthreads();
   const int bmin = sh_minmax[0], bmax = sh_minmax[1];
   if (!FILL && DIR == 0 && tid == 0) p.qs_off[own + 1] = nslices_here;
+  // the block's slice list is complete (the barrier above also makes its
+  // global writes visible to the whole workgroup); it is only whole when the
+  // lists fit the buffer, which the scan launch has decided
+  if (FILL && DIR == 0 && (h->status & FFA_META_ERR_CAPACITY) == 0)
+    validate_pairs(p, p.var + qs_base, nslices_here, a0, a1);
 
   int64_t area = 0;
   for (int cb0 = bmin; cb0 <= bmax; cb0 += CH) {
@@ -441,18 +496,19 @@ __device__ void schedule_block(void* meta, int which, int blk) {
 }
 
 // Counting launch: blocks [0, nq_f) count q2k owners, the next nk_b count k2q
-// owners, the rest validate 16 x 16 tiles of slice pairs.
+// owners, the rest check the slices' bounds and types (MT slices each).
 __global__ __launch_bounds__(MT) void meta_count_kernel(void* meta, int nq, int nk) {
   __shared__ TilesLds sm;
   const int b = blockIdx.x;
   if (b < nq) tiles_block<0, false>(meta, b, sm);
   else if (b < nq + nk) tiles_block<1, false>(meta, b - nq, sm);
-  else validate_tile(meta, b - nq - nk);
+  else check_slices(meta, b - nq - nk);
 }
 
-// Filling launch: blocks [0, nq_f) fill q2k lists, the next nk_b fill k2q
-// lists, the rest rank owners for the longest-first schedules (ns blocks per
-// direction).
+// Filling launch: blocks [0, nq_f) fill q2k lists and test the disjointness
+// of the slice pairs whose common rows begin in their block, the next nk_b
+// fill k2q lists, the rest rank owners for the longest-first schedules (ns
+// blocks per direction).
 __global__ __launch_bounds__(MT) void meta_fill_kernel(void* meta, int nq, int nk, int ns) {
   __shared__ TilesLds sm;
   const int b = blockIdx.x;
@@ -479,9 +535,10 @@ hipError_t launch_build_meta(const int32_t* d_slices, int32_t S, int32_t Tq, int
   for (int i = 0; i < 9; ++i) ia.byte_off[i] = L.byte_off[i];
   const int n5 = 5 * S;
   const int gi = n5 > 0 ? min(1024, (n5 + 255) / 256) : 1;
-  // four launches: init | validate + count | scan | fill + schedule
+  // four launches: init | count + slice checks | scan | fill + pair checks +
+  // schedule
   meta_init_kernel<<<gi, 256, 0, stream>>>(d_slices, d_meta, ia);
-  const int nv = S > 0 ? ((S + 15) / 16) * ((S + 15) / 16) : 0;
+  const int nv = (S + MT - 1) / MT;
   if (L.nq_f + L.nk_b + nv > 0)
     meta_count_kernel<<<L.nq_f + L.nk_b + nv, MT, 0, stream>>>(d_meta, L.nq_f, L.nk_b);
   meta_scan_kernel<<<1, 1024, 0, stream>>>(d_meta);

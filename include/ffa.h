@@ -152,7 +152,13 @@ FFA_API ffa_status ffa_block_meta_workspace_size(int32_t num_slices, int32_t seq
  * the mirror, key columns past seqlen_k ignored, query rows past seqlen_q
  * invalid.  Per block the Full and Partial lists are kept apart, ascending
  * (full_block_offset / mask_block_offset and the k2q mirrors).  The table is
- * validated on the device (bounds, type, disjointness) into the status word.
+ * validated on the device (bounds, type, disjointness) into the status word;
+ * disjointness is tested for the slice pairs that share a 128-row query
+ * block, in time proportional to the sum over query blocks of the square of
+ * the slices meeting the block (linear in the table when each row meets a
+ * bounded number of slices), and only when the lists fit the buffer
+ * (otherwise FFA_META_ERR_CAPACITY is set and the table is not checked for
+ * overlap).
  * The buffer can be reused by any number of ffa_fwd / ffa_bwd calls with the
  * same seqlens and head_dim until it is rebuilt. */
 FFA_API ffa_status ffa_build_block_meta(const int32_t* d_slices, int32_t num_slices,

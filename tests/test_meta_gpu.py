@@ -139,3 +139,66 @@ def test_meta_and_attention_with_thousands_of_slices():
     from tests.test_attention_gpu import full_check
     c = wl.Call(sl, T, T, 2, 1, 64)
     full_check(c, wl.make_tensors(c, 5))
+
+
+def test_meta_overlap_flag_random_tables():
+    """The disjointness test on random small tables of every mask type (many
+    overlapping, many touching along a diagonal, Lq != Lk): the status word
+    equals the oracle's flags table by table."""
+    rng = random.Random(1234)
+    seen = [0, 0]
+    for n in range(1500):
+        T = rng.choice([8, 40, 200, 700])
+        sl = []
+        for _ in range(rng.randint(2, 4)):
+            a, b = sorted(rng.sample(range(T + 1), 2))
+            c, d = sorted(rng.sample(range(T + 1), 2))
+            sl.append((a, b, c, d, rng.randint(0, 3)))
+        m = ffa.build_meta(sl, T, T, 64, validate=False)
+        want = orc.validate(sl, T, T)
+        assert m.status() == want, (n, T, sl)
+        seen[want != 0] += 1
+    _say(f"tables with an overlap: {seen[1]}, without: {seen[0]}")
+    assert min(seen) > 300
+
+
+def _causal_and_strict_upper(lens):
+    """Per sequence a CAUSAL slice and an INV_CAUSAL slice one key to the
+    right over one row less: the strict upper triangle.  The two share their
+    bounding box but no (query, key) pair."""
+    sl, s = [], 0
+    for L in lens:
+        sl.append((s, s + L, s, s + L, wl.CAUSAL))
+        if L > 1:
+            sl.append((s, s + L - 1, s + 1, s + L, wl.INV_CAUSAL))
+        s += L
+    return sl, s
+
+
+def test_meta_validation_ten_thousand_slices():
+    """A table of 10,000 slices whose pairs share bounding boxes but not valid
+    pairs (status 0, as the oracle finds), then the same table with one
+    planted overlap, one out-of-bounds slice and one bad type: the status
+    word equals the oracle's flags in each case."""
+    rng = random.Random(77)
+    lens = [rng.randint(2, 24) for _ in range(5000)]
+    sl, T = _causal_and_strict_upper(lens)
+    assert len(sl) == 10000
+    _say(f"{len(sl)} slices over {T} tokens")
+    m = ffa.build_meta(sl, T, T, 128, validate=False)
+    assert orc.validate(sl, T, T) == 0
+    assert m.status() == 0
+    # the two slices of a sequence tile its square exactly
+    assert m.area() == orc.total_area(sl) == sum(L * L for L in lens)
+    # one INV_CAUSAL slice moved onto its sequence's diagonal
+    i = 2 * 2500 + 1
+    q0, q1, k0, k1, t = sl[i]
+    bad = list(sl)
+    bad[i] = (q0, q1, k0 - 1, k1 - 1, t)
+    assert orc.validate(bad, T, T) == orc.ERR_OVERLAP
+    assert ffa.build_meta(bad, T, T, 128, validate=False).status() == orc.ERR_OVERLAP
+    # plus a slice past the end and one of an unknown type
+    worse = bad + [(T - 4, T + 1, 0, 4, wl.FULL), (0, 1, T - 1, T, 7)]
+    want = orc.validate(worse, T, T)
+    assert want == orc.ERR_OVERLAP | orc.ERR_BOUNDS | orc.ERR_TYPE
+    assert ffa.build_meta(worse, T, T, 128, validate=False).status() == want
