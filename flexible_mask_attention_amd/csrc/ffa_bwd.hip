@@ -315,7 +315,7 @@ __global__ __launch_bounds__(NT, 3) __attribute__((amdgpu_waves_per_eu(3, 3))) v
       if (masked) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (!((w >> (8 * (r >> 2) + (r & 3))) & 1u)) sacc[r] = -INFINITY;
+          sacc[r] = keep_or_neg_inf(sacc[r], w, 8 * (r >> 2) + (r & 3));
       }
 
 #pragma unroll

@@ -216,7 +216,7 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         const uint32_t w = static_cast<uint32_t>(mk >> (32 * qb));
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (!((w >> (8 * (r >> 2) + (r & 3))) & 1u)) sacc[r] = -INFINITY;
+          sacc[r] = keep_or_neg_inf(sacc[r], w, 8 * (r >> 2) + (r & 3));
       }
 
       // P = exp2(S c - LSE log2 e), dS = P (dP - D)

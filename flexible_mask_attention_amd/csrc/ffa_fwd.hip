@@ -187,7 +187,7 @@ void ffa_fwd_kernel(FwdArgs a) {
       if (masked) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (!((w >> (8 * (r >> 2) + (r & 3))) & 1u)) sacc[r] = -INFINITY;
+          sacc[r] = keep_or_neg_inf(sacc[r], w, 8 * (r >> 2) + (r & 3));
       }
       bf16x8 pop[2];
       float psum = 0.f;

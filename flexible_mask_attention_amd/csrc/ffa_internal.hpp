@@ -178,6 +178,14 @@ __device__ __forceinline__ uint64_t bit_range(int a, int b) {
   return (~0ull >> (63 - (b - a))) << a;
 }
 
+// x where bit b of w is set, else -inf: the one-bit field sign-extended
+// (v_bfe_i32) selects between the two bit patterns in one three-input bitwise
+// operation, with no condition register and so no wait states after it
+__device__ __forceinline__ float keep_or_neg_inf(float x, uint32_t w, int b) {
+  const uint32_t m = static_cast<uint32_t>(__builtin_amdgcn_sbfe(static_cast<int>(w), b, 1));
+  return __uint_as_float((__float_as_uint(x) & m) | (~m & 0xff800000u));
+}
+
 // bits [a, b] of a 32-bit word (0 <= a <= b <= 31)
 __device__ __forceinline__ uint32_t bit_range32(int a, int b) {
   return (~0u >> (31 - (b - a))) << a;
