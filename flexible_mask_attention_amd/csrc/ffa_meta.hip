@@ -299,8 +299,11 @@ __device__ void tiles_block(void* meta, int own, TilesLds& sm) {
   int64_t area = 0;
   for (int cb0 = bmin; cb0 <= bmax; cb0 += CH) {
     const int cb1 = min(cb0 + CH, bmax + 1);   // blocks [cb0, cb1)
-    for (int i = tid; i < CH + 1; i += MT) {
-      if (i < CH) cnt[i] = 0;
+    const int nb = cb1 - cb0;
+    // only the chunk's nb entries are used (intervals write below nb); the
+    // rest of the arrays is never read
+    for (int i = tid; i < nb; i += MT) {
+      cnt[i] = 0;
       diff[i] = 0;
     }
     __syncthreads();
@@ -349,16 +352,16 @@ __device__ void tiles_block(void* meta, int own, TilesLds& sm) {
     // prefix sum of diff over the chunk: thread tid owns PER consecutive blocks
     int run = 0;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) run += diff[tid * PER + e];
+    for (int e = 0; e < PER; ++e) run += (tid * PER + e < nb) ? diff[tid * PER + e] : 0;
     int dummy;
     int carry = block_exclusive_scan(run, ws, &dummy);
     int nf = 0, np = 0;
     int vals[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-      carry += diff[tid * PER + e];
       const int b = tid * PER + e;
-      const int v = (b < cb1 - cb0) ? cnt[b] + carry : 0;
+      carry += (b < nb) ? diff[b] : 0;
+      const int v = (b < nb) ? cnt[b] + carry : 0;
       vals[e] = v;
       area += v;
       nf += (v != 0 && v == cap);
@@ -409,44 +412,49 @@ __device__ void tiles_block(void* meta, int own, TilesLds& sm) {
   }
 }
 
-// Turn the per-owner counts stored at [1..n] into offsets (in place) and lay
-// out the variable region.  One block of 1024 threads.
-__device__ void scan_inplace(int32_t* a, int n, int* ws) {
-  // a[0] = 0; inclusive scan of a[1..n]
-  const int tid = threadIdx.x, NT = blockDim.x;
-  const int lane = tid & 63, w = tid >> 6;
-  if (tid == 0) a[0] = 0;
-  int carry = 0;
-  for (int base = 1; base <= n; base += NT) {
-    const int i = base + tid;
-    int x = (i <= n) ? a[i] : 0;
-    int incl = x;
-    for (int o = 1; o < 64; o <<= 1) {
-      int y = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += y;
-    }
-    if (lane == 63) ws[w] = incl;
-    __syncthreads();
-    int pre = 0, tot = 0;
-    for (int j = 0; j < NT / 64; ++j) {
-      if (j < w) pre += ws[j];
-      tot += ws[j];
-    }
-    if (i <= n) a[i] = carry + pre + incl;
-    carry += tot;
-    __syncthreads();
-  }
-}
 
+// The five offset arrays (counts stored at [1..n]) turned into offsets in
+// place, all five per chunk of blockDim.x entries: the chunk's values of every
+// array are loaded before any is scanned, so a chunk waits for memory once,
+// not five times.
 __global__ void meta_scan_kernel(void* meta) {
-  __shared__ int ws[16];
+  __shared__ int ws[5][16];
   MetaPtrs p = meta_ptrs(meta);
   MetaHeader* h = p.hdr;
-  scan_inplace(p.qf_off, h->nq_f, ws);
-  scan_inplace(p.qm_off, h->nq_f, ws);
-  scan_inplace(p.kf_off, h->nk_b, ws);
-  scan_inplace(p.km_off, h->nk_b, ws);
-  scan_inplace(p.qs_off, h->nq_f, ws);
+  int32_t* const arr[5] = {p.qf_off, p.qm_off, p.kf_off, p.km_off, p.qs_off};
+  const int len[5] = {h->nq_f, h->nq_f, h->nk_b, h->nk_b, h->nq_f};
+  const int tid = threadIdx.x, NT = blockDim.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int nmax = max(h->nq_f, h->nk_b);
+  if (tid == 0)
+    for (int k = 0; k < 5; ++k) arr[k][0] = 0;
+  int carry[5] = {0, 0, 0, 0, 0};
+  for (int base = 1; base <= nmax; base += NT) {
+    const int i = base + tid;
+    int incl[5];
+#pragma unroll
+    for (int k = 0; k < 5; ++k) incl[k] = (i <= len[k]) ? arr[k][i] : 0;
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl[k], o, 64);
+        if (lane >= o) incl[k] += y;
+      }
+      if (lane == 63) ws[k][w] = incl[k];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+      int pre = 0, tot = 0;
+      for (int q = 0; q < NT / 64; ++q) {
+        if (q < w) pre += ws[k][q];
+        tot += ws[k][q];
+      }
+      if (i <= len[k]) arr[k][i] = carry[k] + pre + incl[k];
+      carry[k] += tot;
+    }
+    __syncthreads();
+  }
   __syncthreads();
   if (threadIdx.x == 0) {
     const int64_t n0 = p.qf_off[h->nq_f], n1 = p.qm_off[h->nq_f];
@@ -536,7 +544,7 @@ hipError_t launch_build_meta(const int32_t* d_slices, int32_t S, int32_t Tq, int
   const int n5 = 5 * S;
   const int gi = n5 > 0 ? min(1024, (n5 + 255) / 256) : 1;
   // four launches: init | count + slice checks | scan | fill + pair checks +
-  // schedule
+  // schedules
   meta_init_kernel<<<gi, 256, 0, stream>>>(d_slices, d_meta, ia);
   const int nv = (S + MT - 1) / MT;
   if (L.nq_f + L.nk_b + nv > 0)
