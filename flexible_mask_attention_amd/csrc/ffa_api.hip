@@ -60,10 +60,11 @@ ffa_status check_shape(const ffa_shape* s) {
 
 namespace {
 
-// Backward workspace: -D and LSE log2 e rows, then the split counters and the
-// split partial sums of the dK/dV kernel, each 256-byte aligned.
+// Backward workspace: -D, LSE log2 e and -LSE / scale rows, then the split
+// counters and the split partial sums of the dK/dV kernel, each 256-byte
+// aligned.
 struct BwdWsLayout {
-  int64_t lvec, cnt, part, total;
+  int64_t lvec, mvec, cnt, part, total;
   int32_t split_e;
 };
 
@@ -74,7 +75,8 @@ BwdWsLayout bwd_ws_layout(const ffa_shape& s) {
   W.split_e = split_candidates(s.num_heads_kv, nk_b);
   const int64_t nc = (int64_t)W.split_e * s.num_heads_kv;
   W.lvec = rows;
-  W.cnt = 2 * rows;
+  W.mvec = 2 * rows;
+  W.cnt = 3 * rows;
   W.part = W.cnt + align256(4 * nc);
   W.total = W.part + nc * 2 * 2 * BN_B * (int64_t)s.head_dim * 4;
   return W;
@@ -325,6 +327,7 @@ FFA_API ffa_status ffa_bwd_grouped(const ffa_shape* shape, ffa_tensor_in q, ffa_
   char* ws = static_cast<char*>(d_ws);
   a.dvec = reinterpret_cast<float*>(ws);
   a.lvec = reinterpret_cast<float*>(ws + W.lvec);
+  a.mvec = reinterpret_cast<float*>(ws + W.mvec);
   a.split_cnt = reinterpret_cast<int32_t*>(ws + W.cnt);
   a.split_part = reinterpret_cast<float*>(ws + W.part);
   a.split_e = W.split_e;

@@ -53,6 +53,7 @@ __global__ __launch_bounds__(NT) void ffa_bwd_pre_kernel(BwdArgs a) {
     a.dvec[(int64_t)h * a.Tq + i] = -acc;
     const float l = a.lse[(int64_t)h * a.Tq + i];
     a.lvec[(int64_t)h * a.Tq + i] = (l == -INFINITY) ? 0.f : l * LOG2E;
+    a.mvec[(int64_t)h * a.Tq + i] = (l == -INFINITY) ? 0.f : -l / a.scale;
   }
 }
 
@@ -210,6 +211,7 @@ __global__ __launch_bounds__(NT, 3) __attribute__((amdgpu_waves_per_eu(3, 3))) v
       if (h32 == 0) {
         a.dvec[(int64_t)head * a.Tq + qrow] = ndval;
         a.lvec[(int64_t)head * a.Tq + qrow] = l2;
+        a.mvec[(int64_t)head * a.Tq + qrow] = (l == -INFINITY) ? 0.f : -l / a.scale;
       }
     }
   } else {

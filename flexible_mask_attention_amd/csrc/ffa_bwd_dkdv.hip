@@ -101,7 +101,7 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     dq_dma.load(a.q + (int64_t)hq * a.q_hs, a.q_ts, m * BM_B, vr, st);
     dg_dma.load(a.dout + (int64_t)hq * a.do_hs, a.do_ts, m * BM_B, vr, st + TILE_B);
     if (wid < 2) {
-      const float* src = (wid == 0 ? a.lvec : a.dvec) + (int64_t)hq * a.Tq + m * BM_B;
+      const float* src = (wid == 0 ? a.mvec : a.dvec) + (int64_t)hq * a.Tq + m * BM_B;
       const int rows = vr < 0 ? 0 : (vr > BM_B ? BM_B : vr);
       const i32x4 r = make_rsrc(src, (uint32_t)(rows * 4));
       dma4(r, st + 2 * TILE_B + wid * BM_B * 4, lane * 4);
@@ -191,16 +191,22 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       if (masked && __ballot(((mkf >> (32 * qb)) & 0xffffffffull) != 0) == 0) continue;
-      // S = Q K^T and dP - D = dO V^T - D; lane = key, registers = rows
-      // 32qb + 8(r/4) + 4*h32 + r%4.  The dP accumulator starts at -D (four
-      // 128-bit LDS reads), which saves the subtraction in dS = P (dP - D).
-      f32x16 sacc = f32x16{}, pacc;
+      // S - LSE / scale = Q K^T - LSE / scale and dP - D = dO V^T - D; lane =
+      // key, registers = rows 32qb + 8(r/4) + 4*h32 + r%4.  Both accumulators
+      // start at their row statistic (four 128-bit LDS reads each, issued
+      // before the MFMAs): P = exp2(c (S - LSE / scale)) = exp2(S c - LSE
+      // log2 e) then needs one multiply, and dS = P (dP - D) no subtraction.
+      f32x16 sacc, pacc;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const f32x4 nd = *(const __attribute__((address_space(3))) f32x4*)(
             lb + laddr + (32 * qb + 8 * j) * 4 + BM_B * 4);
+        const f32x4 nm = *(const __attribute__((address_space(3))) f32x4*)(lb + laddr + (32 * qb + 8 * j) * 4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pacc[4 * j + i] = nd[i];
+        for (int i = 0; i < 4; ++i) {
+          pacc[4 * j + i] = nd[i];
+          sacc[4 * j + i] = nm[i];
+        }
       }
 #pragma unroll
       for (int k = 0; k < KS; ++k) {
@@ -219,17 +225,12 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
           sacc[r] = keep_or_neg_inf(sacc[r], w, 8 * (r >> 2) + (r & 3));
       }
 
-      // P = exp2(S c - LSE log2 e), dS = P (dP - D)
+      // P = exp2(c (S - LSE / scale)), dS = P (dP - D)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 l4 = *(const __attribute__((address_space(3))) f32x4*)(lb + laddr + (32 * qb + 8 * j) * 4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * j + i;
-          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -l4[i]));
-          sacc[r] = pv;
-          pacc[r] *= pv;
-        }
+      for (int r = 0; r < 16; ++r) {
+        const float pv = __builtin_amdgcn_exp2f(sacc[r] * c);
+        sacc[r] = pv;
+        pacc[r] *= pv;
       }
 
       // dV^T += dO^T P and dK^T += Q^T dS over the half's two 16-row chunks

@@ -389,6 +389,7 @@ struct BwdArgs {
   const float* lse;
   float* dvec;        // workspace: -D_i = -dO_i . O_i, [Hq][Tq]
   float* lvec;        // workspace: LSE_i * log2(e) (0 where LSE = -inf), [Hq][Tq]
+  float* mvec;        // workspace: -LSE_i / scale (0 where LSE = -inf), [Hq][Tq]
   __bf16* dq;
   __bf16* dk;
   __bf16* dv;

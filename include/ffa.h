@@ -200,6 +200,7 @@ FFA_API ffa_status ffa_fwd(const ffa_shape* shape, ffa_tensor_in q, ffa_tensor_i
  * boundary of d_ws:
  *   -D_i = -(dO_i . O_i)      fp32 [num_heads_q][seqlen_q]
  *   LSE_i * log2(e)           fp32 [num_heads_q][seqlen_q]
+ *   -LSE_i / softmax_scale    fp32 [num_heads_q][seqlen_q]
  *   split finish counters     int32 [E][num_heads_kv]
  *   split partial dK, dV      fp32 [E][num_heads_kv][2 halves][dK, dV][128 * head_dim]
  * with E = min(ceil(seqlen_k / 128), min(32, max(4, 128 / num_heads_kv))) key

@@ -95,11 +95,11 @@ def test_host_validation_returns_before_enqueue():
     assert L.ffa_fwd(None, good, good, good, meta, goodo, lse, None) == 1
     # backward workspace too small / null
     ws = ctypes.c_size_t()
-    # -D and LSE log2 e rows (2 x 2 KB), the split counters of 2 candidate key
-    # blocks x 2 kv heads (one 256-byte line) and their fp32 partials
-    # (2 halves x (dK, dV) x 128 keys x 64)
+    # -D, LSE log2 e and -LSE / scale rows (3 x 2 KB), the split counters of 2
+    # candidate key blocks x 2 kv heads (one 256-byte line) and their fp32
+    # partials (2 halves x (dK, dV) x 128 keys x 64)
     assert L.ffa_bwd_workspace_size(P(_shape()), P(ws)) == 0
-    assert ws.value == 2 * (2 * 256 * 4) + 256 + 2 * 2 * (2 * 2 * 128 * 64 * 4)
+    assert ws.value == 3 * (2 * 256 * 4) + 256 + 2 * 2 * (2 * 2 * 128 * 64 * 4)
     assert L.ffa_bwd(P(_shape()), good, good, good, good, lse, good, meta, goodo, goodo, goodo,
                      0x100000, ws.value - 1, None) == 3
     assert L.ffa_bwd(P(_shape()), good, good, good, good, lse, good, meta, goodo, goodo, goodo,

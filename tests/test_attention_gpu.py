@@ -224,7 +224,7 @@ def _ws_layout(Tq, Tk, Hq, Hkv, d):
     a256 = lambda x: (x + 255) // 256 * 256          # noqa: E731
     rows = a256(4 * Hq * Tq)
     E = min(-(-Tk // 128), min(32, max(4, 128 // Hkv)))
-    cnt = 2 * rows
+    cnt = 3 * rows                                    # -D, LSE log2 e, -LSE / scale
     part = cnt + a256(4 * E * Hkv)
     return {"E": E, "cnt": cnt, "part": part, "end": part + E * Hkv * 2 * 2 * 128 * d * 4}
 
