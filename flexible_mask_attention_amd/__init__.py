@@ -64,7 +64,7 @@ class MetaView(ctypes.Structure):
         (n, ctypes.c_void_p) for n in (
             "status", "area", "full_block_offset", "mask_block_offset", "k2q_full_block_offset",
             "k2q_mask_block_offset", "qblock_slice_offset", "schedule_fwd", "schedule_bwd",
-            "index_base", "list_offsets")]
+            "index_base", "list_offsets", "block_records_fwd", "block_records_bwd")]
 
 
 _lib_handle = None
@@ -241,6 +241,8 @@ class BlockMeta:
             "qblock_slice_offset": qs, "qblock_slice_idx": lst(4, int(qs[-1])),
             "schedule_fwd": self._read(v.schedule_fwd, nqf, torch.int32).long(),
             "schedule_bwd": self._read(v.schedule_bwd, nkb, torch.int32).long(),
+            "records_fwd": self._read(v.block_records_fwd, 16 * nqf, torch.int32).long().view(nqf, 16),
+            "records_bwd": self._read(v.block_records_bwd, 16 * nkb, torch.int32).long().view(nkb, 16),
             "tiles": (v.bm_fwd, v.bn_fwd, v.bm_bwd, v.bn_bwd),
         }
 

@@ -189,6 +189,8 @@ FFA_API ffa_status ffa_block_meta_view(const void* d_meta, int32_t num_slices, i
   out->schedule_fwd = reinterpret_cast<const int32_t*>(b + L.byte_off[A_SCHED_F]);
   out->schedule_bwd = reinterpret_cast<const int32_t*>(b + L.byte_off[A_SCHED_B]);
   out->index_base = reinterpret_cast<const int32_t*>(b + L.byte_off[A_VAR]);
+  out->block_records_fwd = reinterpret_cast<const int32_t*>(b + L.byte_off[A_REC_F]);
+  out->block_records_bwd = reinterpret_cast<const int32_t*>(b + L.byte_off[A_REC_B]);
   return FFA_OK;
 }
 
@@ -243,6 +245,7 @@ FFA_API ffa_status ffa_fwd_grouped(const ffa_shape* shape, ffa_tensor_in q, ffa_
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.nitems = L.nq_f;
+  a.rec_off = L.byte_off[A_REC_F];
   a.scale = shape->softmax_scale;
   a.scale_log2 = shape->softmax_scale * LOG2E;
   a.flags = flags;
@@ -361,6 +364,8 @@ FFA_API ffa_status ffa_bwd_grouped(const ffa_shape* shape, ffa_tensor_in q, ffa_
   a.Hkv = Hkv;
   a.nq_f = L.nq_f;
   a.nk_b = L.nk_b;
+  a.rec_off_f = L.byte_off[A_REC_F];
+  a.rec_off_b = L.byte_off[A_REC_B];
   a.scale = shape->softmax_scale;
   a.scale_log2 = shape->softmax_scale * LOG2E;
   a.flags = flags;

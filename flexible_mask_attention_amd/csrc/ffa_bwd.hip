@@ -161,18 +161,21 @@ __global__ __launch_bounds__(NT, 3) __attribute__((amdgpu_waves_per_eu(3, 3))) v
   const int kvh = head / (a.Hq / a.Hkv);
   const MetaView mv = meta_view(group_meta(a.groups, kvh));
   const FFA_CONST MetaHeader* hd = mv.hdr;
-  if (hd->status != 0 || hd->seqlen_q != a.Tq || hd->seqlen_k != a.Tk) return;
-  const int m = mv.sched_f[item];
+  if (!meta_usable(hd, a.Tq, a.Tk, A_REC_F, a.rec_off_f)) return;
+  // the item's block record (one read), as in the forward
+  cint32_t* rec = (cint32_t*)((const FFA_CONST char*)hd + a.rec_off_f) + REC * item;
+  const int m = rec[R_OWNER];
   const int qrow = m * BM_F + wid * 32 + l32;
   const bool qok = qrow < a.Tq;
 
-  const int f0 = mv.qf_off[m], nF = mv.qf_off[m + 1] - f0;
-  const int p0 = mv.qm_off[m], nP = mv.qm_off[m + 1] - p0;
+  const int f0 = rec[R_F0], nF = rec[R_NF];
+  const int p0 = rec[R_P0], nP = rec[R_NP];
   const int nU = HALVES * (nP + nF);            // stages
   cint32_t* fidx = mv.var + hd->list_off[L_QF] + f0;
   cint32_t* pidx = mv.var + hd->list_off[L_QM] + p0;
-  const int s0 = mv.qs_off[m], nS = mv.qs_off[m + 1] - s0;
+  const int s0 = rec[R_S0], nS = rec[R_NS];
   cint32_t* sidx = mv.var + hd->list_off[L_QS] + s0;
+  const int tile0 = nP > 0 ? rec[R_TP] : rec[R_TF];   // Partial tiles come first
 
   bf16x8 qop[KS], gop[KS];
   {
@@ -248,12 +251,13 @@ __global__ __launch_bounds__(NT, 3) __attribute__((amdgpu_waves_per_eu(3, 3))) v
   const __bf16* kbase = a.k + (int64_t)kvh * a.k_hs;
   const __bf16* vbase = a.v + (int64_t)kvh * a.v_hs;
   auto tile_of = [&](int t) { return t < nP ? pidx[t] : fidx[t - nP]; };
-  auto issue = [&](int u, int stage) {
-    const int key0 = tile_of(u / HALVES) * BN_F + (u % HALVES) * SK;
+  auto issue_tile = [&](int tile, int half, int stage) {
+    const int key0 = tile * BN_F + half * SK;
     char* st = smem + stage * STAGE_B;
     if (wid < 2) dm.load(kbase, a.k_ts, key0, a.Tk - key0, st);
     else dm.load(vbase, a.v_ts, key0, a.Tk - key0, st + TILE_B);
   };
+  auto issue = [&](int u, int stage) { issue_tile(tile_of(u / HALVES), u % HALVES, stage); };
 
   f32x16 dqacc[MB];
 #pragma unroll
@@ -348,7 +352,7 @@ __global__ __launch_bounds__(NT, 3) __attribute__((amdgpu_waves_per_eu(3, 3))) v
     __syncthreads();
   };
 
-  if (nU > 0) issue(0, 0);
+  if (nU > 0) issue_tile(tile0, 0, 0);
   wait_dma();
   __syncthreads();
   for (int u = 0; u < nU; u += 2) {

@@ -43,26 +43,25 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   xcd_map(blockIdx.x, a.nk_b + a.split_e, a.Hkv, a.Hkv, item, kvh);
   const MetaView mv = meta_view(group_meta(a.groups, kvh));
   const FFA_CONST MetaHeader* hd = mv.hdr;
-  if (hd->status != 0 || hd->seqlen_q != a.Tq || hd->seqlen_k != a.Tk) return;
+  if (!meta_usable(hd, a.Tq, a.Tk, A_REC_B, a.rec_off_b)) return;
   // Items [0, 2 split_e) are the two halves of the split_e longest blocks (the
   // schedule is longest first); a candidate is split only if its work exceeds
   // what one resident workgroup would get with the whole backward spread
   // evenly, cost * slots > sum over kv heads of their total cost (the query
   // heads per kv head cancel), otherwise its first item does all of it and
   // the second exits.
-  int part = -1, cand = 0, n;
-  if (item < 2 * a.split_e) {
-    cand = item >> 1;
-    n = mv.sched_b[cand];
-  } else {
-    n = mv.sched_b[item - a.split_e];
-  }
+  int part = -1, cand = 0;
+  const int rank = item < 2 * a.split_e ? (cand = item >> 1) : item - a.split_e;
+  // the block record (one read): key block, list offsets and counts, and the
+  // last tile of each list (the walk starts there)
+  cint32_t* rec = (cint32_t*)((const FFA_CONST char*)hd + a.rec_off_b) + REC * rank;
+  const int n = rec[RB_OWNER];
   const int key = n * BN_B + wid * 32 + l32;
   const bool kok = key < a.Tk;
   const int G = a.Hq / a.Hkv;
 
-  const int f0 = mv.kf_off[n], nF = mv.kf_off[n + 1] - f0;
-  const int p0 = mv.km_off[n], nP = mv.km_off[n + 1] - p0;
+  const int f0 = rec[RB_F0], nF = rec[RB_NF];
+  const int p0 = rec[RB_P0], nP = rec[RB_NP];
   const int nT = nP + nF;
   if (item < 2 * a.split_e) {
     const int64_t cost = 4LL * nF + 5LL * nP;
@@ -93,9 +92,8 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   TileDma<D, BM_B> dq_dma, dg_dma;
   dq_dma.init(wid, lane, a.q_ts);
   dg_dma.init(wid, lane, a.do_ts);
-  auto issue = [&](int u, int stage) {
+  auto issue_tile = [&](int u, int m, int stage) {
     const int hq = kvh * G + u % G;
-    const int m = tile_of(nT - 1 - u / G);
     char* st = smem + stage * STAGE_B;
     const int vr = a.Tq - m * BM_B;
     dq_dma.load(a.q + (int64_t)hq * a.q_hs, a.q_ts, m * BM_B, vr, st);
@@ -107,9 +105,12 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
       dma4(r, st + 2 * TILE_B + wid * BM_B * 4, lane * 4);
     }
   };
+  auto issue = [&](int u, int stage) { issue_tile(u, tile_of(nT - 1 - u / G), stage); };
+
   // the first tile's loads go out before the K / V loads, so that the two
-  // memory round trips of the prologue overlap
-  if (ubeg < uend) issue(ubeg, 0);
+  // memory round trips of the prologue overlap; a whole walk starts at the
+  // last list entry, which the record holds
+  if (ubeg < uend) issue_tile(ubeg, ubeg == 0 ? (nF > 0 ? rec[RB_TF] : rec[RB_TP]) : tile_of(nT - 1 - ubeg / G), 0);
 
   // K and V as B operands: lane holds K[key][16k + 8*h32 + e]
   bf16x8 kop[KS], vop[KS];

@@ -42,8 +42,8 @@ struct MetaHeader {
   int64_t area;          // (dev) exact valid-pair count
   int64_t nnz[5];        // (dev) q2k full, q2k mask, k2q full, k2q mask, q-block slices
   int64_t list_off[5];   // (dev) entry offsets of those lists in the variable region
-  int64_t byte_off[9];   // offsets of the fixed arrays (see MetaLayout)
-  int64_t pad1[3];
+  int64_t byte_off[11];  // offsets of the fixed arrays (see MetaLayout)
+  int64_t pad1[1];
 };
 static_assert(sizeof(MetaHeader) <= 256, "header must fit in 256 bytes");
 constexpr int64_t HEADER_BYTES = 256;
@@ -51,15 +51,29 @@ constexpr int64_t HEADER_BYTES = 256;
 enum ListId { L_QF = 0, L_QM = 1, L_KF = 2, L_KM = 3, L_QS = 4 };
 
 // Fixed arrays, in this order after the header (int32, each padded to 256 B):
-//   slices[5*S], q2k_full_off[nq_f+1], q2k_mask_off[nq_f+1],
-//   k2q_full_off[nk_b+1], k2q_mask_off[nk_b+1], qs_off[nq_f+1],
-//   sched_f[nq_f], sched_b[nk_b], then the variable region.
-enum FixedId { A_SLICES = 0, A_QF_OFF, A_QM_OFF, A_KF_OFF, A_KM_OFF, A_QS_OFF, A_SCHED_F,
-               A_SCHED_B, A_VAR };
+//   q2k_full_off[nq_f+1], q2k_mask_off[nq_f+1], k2q_full_off[nk_b+1],
+//   k2q_mask_off[nk_b+1], qs_off[nq_f+1], sched_f[nq_f], sched_b[nk_b],
+//   rec_f[nq_f][REC], rec_b[nk_b][REC], slices[5*S], then the variable region.
+// Everything before the slice copy depends on the sequence lengths only, so
+// the host knows where the block records are without reading the buffer.
+enum FixedId { A_QF_OFF = 0, A_QM_OFF, A_KF_OFF, A_KM_OFF, A_QS_OFF, A_SCHED_F, A_SCHED_B,
+               A_REC_F, A_REC_B, A_SLICES, A_VAR };
+
+// Block record, one per owner in schedule order (int32 each): what a
+// forward / dQ (rec_f) or dK/dV (rec_b) workgroup needs before its first tile
+// load, in one 64-byte read.
+//   rec_f: owner q-block, q2k Full list offset and count, Partial list offset
+//          and count, slice list offset and count, first Full tile, first
+//          Partial tile (-1 when the list is empty)
+//   rec_b: owner k-block, k2q Full list offset and count, Partial list offset
+//          and count, last Full tile, last Partial tile (-1 when empty)
+constexpr int REC = 16;
+enum RecField { R_OWNER = 0, R_F0, R_NF, R_P0, R_NP, R_S0, R_NS, R_TF, R_TP };
+enum RecFieldB { RB_OWNER = 0, RB_F0, RB_NF, RB_P0, RB_NP, RB_TF, RB_TP };
 
 struct MetaLayout {
   int32_t nq_f, nk_f, nq_b, nk_b;
-  int64_t byte_off[9];
+  int64_t byte_off[11];
   int64_t fixed_bytes;
 };
 
@@ -72,10 +86,11 @@ inline MetaLayout meta_layout(int32_t S, int32_t Tq, int32_t Tk) {
   L.nk_f = cdiv(Tk, BN_F);
   L.nq_b = cdiv(Tq, BM_B);
   L.nk_b = cdiv(Tk, BN_B);
-  const int64_t counts[8] = {5LL * S, L.nq_f + 1LL, L.nq_f + 1LL, L.nk_b + 1LL, L.nk_b + 1LL,
-                             L.nq_f + 1LL, (int64_t)L.nq_f, (int64_t)L.nk_b};
+  const int64_t counts[10] = {L.nq_f + 1LL, L.nq_f + 1LL, L.nk_b + 1LL, L.nk_b + 1LL,
+                              L.nq_f + 1LL, (int64_t)L.nq_f, (int64_t)L.nk_b,
+                              (int64_t)REC * L.nq_f, (int64_t)REC * L.nk_b, 5LL * S};
   int64_t off = HEADER_BYTES;
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 10; ++i) {
     L.byte_off[i] = off;
     off += align256(4 * counts[i]);
   }
@@ -100,8 +115,21 @@ struct MetaView {
   cint32_t* qs_off;
   cint32_t* sched_f;
   cint32_t* sched_b;
+  cint32_t* rec_f;
+  cint32_t* rec_b;
   cint32_t* var;
 };
+
+// The checks a workgroup makes before it reads a metadata buffer: built
+// without error and for these sequence lengths, which also places the block
+// records where the host expects them (rec_id, at byte offset rec_off).  The
+// four header words are compared without short-circuit so that they are read
+// in one round trip.
+__device__ inline bool meta_usable(const FFA_CONST MetaHeader* hd, int Tq, int Tk, int rec_id,
+                                   int64_t rec_off) {
+  return ((hd->status == 0) & (hd->seqlen_q == Tq) & (hd->seqlen_k == Tk) &
+          (hd->byte_off[rec_id] == rec_off)) != 0;
+}
 
 __device__ inline MetaView meta_view(const void* meta) {
   MetaView v;
@@ -115,6 +143,8 @@ __device__ inline MetaView meta_view(const void* meta) {
   v.qs_off = (cint32_t*)(b + v.hdr->byte_off[A_QS_OFF]);
   v.sched_f = (cint32_t*)(b + v.hdr->byte_off[A_SCHED_F]);
   v.sched_b = (cint32_t*)(b + v.hdr->byte_off[A_SCHED_B]);
+  v.rec_f = (cint32_t*)(b + v.hdr->byte_off[A_REC_F]);
+  v.rec_b = (cint32_t*)(b + v.hdr->byte_off[A_REC_B]);
   v.var = (cint32_t*)(b + v.hdr->byte_off[A_VAR]);
   return v;
 }
@@ -374,6 +404,7 @@ struct FwdArgs {
   int64_t q_ts, q_hs, k_ts, k_hs, v_ts, v_hs, o_ts, o_hs;
   int32_t Tq, Tk, Hq, Hkv;
   int32_t nitems;     // query blocks (the grid is nitems * Hq)
+  int64_t rec_off;    // byte offset of the forward block records in metadata of these lengths
   float scale_log2;   // softmax_scale * log2(e)
   float scale;
   uint32_t flags;     // FFA_ACCUMULATE: merge into the (o, lse) already in the buffers
@@ -398,6 +429,7 @@ struct BwdArgs {
   int64_t dq_ts, dq_hs, dk_ts, dk_hs, dv_ts, dv_hs;
   int32_t Tq, Tk, Hq, Hkv;
   int32_t nq_f, nk_b; // query blocks of the dQ grid, key blocks of the dK/dV grid
+  int64_t rec_off_f, rec_off_b;   // byte offsets of the block records in metadata of these lengths
   float scale_log2;
   float scale;
   uint32_t flags;     // FFA_ACCUMULATE: add to the dq / dk / dv already in the buffers

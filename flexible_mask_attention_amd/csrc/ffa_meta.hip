@@ -30,6 +30,8 @@ namespace {
 constexpr int MT = 256;     // threads of the tile kernels
 constexpr int CH = 4096;    // iterated blocks per LDS chunk
 constexpr int PER = CH / MT;
+// owners past MAX_SORT keep their natural order in the schedules
+constexpr int MAX_SORT = 32768;
 
 struct MetaPtrs {
   MetaHeader* hdr;
@@ -41,6 +43,8 @@ struct MetaPtrs {
   int32_t* qs_off;
   int32_t* sched_f;
   int32_t* sched_b;
+  int32_t* rec_f;
+  int32_t* rec_b;
   int32_t* var;
 };
 
@@ -56,6 +60,8 @@ __device__ MetaPtrs meta_ptrs(void* meta) {
   p.qs_off = reinterpret_cast<int32_t*>(b + p.hdr->byte_off[A_QS_OFF]);
   p.sched_f = reinterpret_cast<int32_t*>(b + p.hdr->byte_off[A_SCHED_F]);
   p.sched_b = reinterpret_cast<int32_t*>(b + p.hdr->byte_off[A_SCHED_B]);
+  p.rec_f = reinterpret_cast<int32_t*>(b + p.hdr->byte_off[A_REC_F]);
+  p.rec_b = reinterpret_cast<int32_t*>(b + p.hdr->byte_off[A_REC_B]);
   p.var = reinterpret_cast<int32_t*>(b + p.hdr->byte_off[A_VAR]);
   return p;
 }
@@ -64,7 +70,7 @@ struct InitArgs {
   int32_t S, Tq, Tk, head_dim;
   int32_t nq_f, nk_f, nq_b, nk_b;
   int64_t capacity;
-  int64_t byte_off[9];
+  int64_t byte_off[11];
 };
 
 // Header fields, counters, and a copy of the slice table.
@@ -94,7 +100,7 @@ __global__ void meta_init_kernel(const int32_t* __restrict__ slices, void* meta,
       h->nnz[i] = 0;
       h->list_off[i] = 0;
     }
-    for (int i = 0; i < 9; ++i) h->byte_off[i] = a.byte_off[i];
+    for (int i = 0; i < 11; ++i) h->byte_off[i] = a.byte_off[i];
   }
   int32_t* dst = reinterpret_cast<int32_t*>(b + a.byte_off[A_SLICES]);
   const int n = 5 * a.S;
@@ -389,6 +395,47 @@ __device__ void tiles_block(void* meta, int own, TilesLds& sm) {
     out_p += tp;
     __syncthreads();
   }
+  if (FILL) {
+    // This owner's place in the longest-first schedule (owners with more work
+    // first, ties by index; work = 4 per Full tile + 5 per Partial tile),
+    // counted by all threads over all owners, and its block record.
+    const int n = DIR == 0 ? h->nq_f : h->nk_b;
+    auto cost = [&](int x) { return 4 * (full_off[x + 1] - full_off[x]) + 5 * (mask_off[x + 1] - mask_off[x]); };
+    const int c = cost(own);
+    int before = 0;
+    if (n <= MAX_SORT)
+      for (int x = tid; x < n; x += MT) {
+        const int cx = cost(x);
+        before += (cx > c) || (cx == c && x < own);
+      }
+    int rank;
+    block_exclusive_scan(before, ws, &rank);
+    if (n > MAX_SORT) rank = own;
+    // (the scan's barriers also make this block's list entries visible here)
+    if (tid == 0) {
+      const int f0 = full_off[own], nF = full_off[own + 1] - f0;
+      const int p0 = mask_off[own], nP = mask_off[own + 1] - p0;
+      const int64_t lf = h->list_off[DIR == 0 ? L_QF : L_KF] + f0;
+      const int64_t lp = h->list_off[DIR == 0 ? L_QM : L_KM] + p0;
+      auto entry = [&](int64_t at) { return at < capacity ? p.var[at] : -1; };
+      int32_t* r = (DIR == 0 ? p.rec_f : p.rec_b) + (int64_t)REC * rank;
+      (DIR == 0 ? p.sched_f : p.sched_b)[rank] = own;
+      r[R_OWNER] = own;
+      r[R_F0] = f0;
+      r[R_NF] = nF;
+      r[R_P0] = p0;
+      r[R_NP] = nP;
+      if (DIR == 0) {
+        r[R_S0] = p.qs_off[own];
+        r[R_NS] = p.qs_off[own + 1] - p.qs_off[own];
+        r[R_TF] = nF > 0 ? entry(lf) : -1;
+        r[R_TP] = nP > 0 ? entry(lp) : -1;
+      } else {
+        r[RB_TF] = nF > 0 ? entry(lf + nF - 1) : -1;
+        r[RB_TP] = nP > 0 ? entry(lp + nP - 1) : -1;
+      }
+    }
+  }
   if (!FILL) {
     if (tid == 0) {
       full_off[own + 1] = out_f;
@@ -474,35 +521,6 @@ __global__ void meta_scan_kernel(void* meta) {
   }
 }
 
-// Longest-first order of owners: rank = number of owners with more work, ties
-// broken by index.  Work = 4 per Full tile + 5 per Partial tile.  Owners past
-// MAX_SORT keep their natural order.
-constexpr int MAX_SORT = 32768;
-
-__device__ void schedule_block(void* meta, int which, int blk) {
-  MetaPtrs p = meta_ptrs(meta);
-  const MetaHeader* h = p.hdr;
-  // which = 0: fwd q-blocks, 1: bwd k-blocks
-  const int n = which == 0 ? h->nq_f : h->nk_b;
-  const int32_t* fo = which == 0 ? p.qf_off : p.kf_off;
-  const int32_t* mo = which == 0 ? p.qm_off : p.km_off;
-  int32_t* out = which == 0 ? p.sched_f : p.sched_b;
-  const int o = blk * MT + threadIdx.x;
-  if (o >= n) return;
-  if (n > MAX_SORT) {
-    out[o] = o;
-    return;
-  }
-  auto cost = [&](int x) { return 4 * (fo[x + 1] - fo[x]) + 5 * (mo[x + 1] - mo[x]); };
-  const int c = cost(o);
-  int rank = 0;
-  for (int x = 0; x < n; ++x) {
-    const int cx = cost(x);
-    rank += (cx > c) || (cx == c && x < o);
-  }
-  out[rank] = o;
-}
-
 // Counting launch: blocks [0, nq_f) count q2k owners, the next nk_b count k2q
 // owners, the rest check the slices' bounds and types (MT slices each).
 __global__ __launch_bounds__(MT) void meta_count_kernel(void* meta, int nq, int nk) {
@@ -513,16 +531,15 @@ __global__ __launch_bounds__(MT) void meta_count_kernel(void* meta, int nq, int 
   else check_slices(meta, b - nq - nk);
 }
 
-// Filling launch: blocks [0, nq_f) fill q2k lists and test the disjointness
-// of the slice pairs whose common rows begin in their block, the next nk_b
-// fill k2q lists, the rest rank owners for the longest-first schedules (ns
-// blocks per direction).
-__global__ __launch_bounds__(MT) void meta_fill_kernel(void* meta, int nq, int nk, int ns) {
+// Filling launch: blocks [0, nq_f) fill q2k lists, test the disjointness of
+// the slice pairs whose common rows begin in their block and place their
+// block in the forward schedule; the next nk_b do the same for the k2q lists
+// and the backward schedule.
+__global__ __launch_bounds__(MT) void meta_fill_kernel(void* meta, int nq, int nk) {
   __shared__ TilesLds sm;
   const int b = blockIdx.x;
   if (b < nq) tiles_block<0, true>(meta, b, sm);
-  else if (b < nq + nk) tiles_block<1, true>(meta, b - nq, sm);
-  else schedule_block(meta, (b - nq - nk) / ns, (b - nq - nk) % ns);
+  else tiles_block<1, true>(meta, b - nq, sm);
 }
 
 }  // namespace
@@ -540,19 +557,18 @@ hipError_t launch_build_meta(const int32_t* d_slices, int32_t S, int32_t Tq, int
   ia.nq_b = L.nq_b;
   ia.nk_b = L.nk_b;
   ia.capacity = capacity;
-  for (int i = 0; i < 9; ++i) ia.byte_off[i] = L.byte_off[i];
+  for (int i = 0; i < 11; ++i) ia.byte_off[i] = L.byte_off[i];
   const int n5 = 5 * S;
   const int gi = n5 > 0 ? min(1024, (n5 + 255) / 256) : 1;
   // four launches: init | count + slice checks | scan | fill + pair checks +
-  // schedules
+  // schedules and block recordss
   meta_init_kernel<<<gi, 256, 0, stream>>>(d_slices, d_meta, ia);
   const int nv = (S + MT - 1) / MT;
   if (L.nq_f + L.nk_b + nv > 0)
     meta_count_kernel<<<L.nq_f + L.nk_b + nv, MT, 0, stream>>>(d_meta, L.nq_f, L.nk_b);
   meta_scan_kernel<<<1, 1024, 0, stream>>>(d_meta);
-  const int ns = (max(L.nq_f, L.nk_b) + MT - 1) / MT;
-  if (L.nq_f + L.nk_b + 2 * ns > 0)
-    meta_fill_kernel<<<L.nq_f + L.nk_b + 2 * ns, MT, 0, stream>>>(d_meta, L.nq_f, L.nk_b, ns);
+  if (L.nq_f + L.nk_b > 0)
+    meta_fill_kernel<<<L.nq_f + L.nk_b, MT, 0, stream>>>(d_meta, L.nq_f, L.nk_b);
   return hipGetLastError();
 }
 

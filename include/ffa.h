@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FFA_ABI_VERSION 5
+#define FFA_ABI_VERSION 6
 
 #if defined(__GNUC__)
 #define FFA_API __attribute__((visibility("default")))
@@ -130,6 +130,14 @@ typedef struct {
   const int64_t* list_offsets;       /* device int64[5]: entry offsets from index_base of
                                         full_block_idx, mask_block_idx, k2q_full_block_idx,
                                         k2q_mask_block_idx, qblock_slice_idx */
+  /* block records, 16 int32 each, in schedule order (the kernels' first read):
+   * fwd: q-block, q2k Full offset, Full count, Partial offset, Partial count,
+   *      slice-list offset, slice count, first Full tile, first Partial tile;
+   * bwd: k-block, k2q Full offset, Full count, Partial offset, Partial count,
+   *      last Full tile, last Partial tile; -1 for a tile of an empty list,
+   *      the rest of the 16 unspecified */
+  const int32_t* block_records_fwd;  /* [num_qblocks_fwd][16] */
+  const int32_t* block_records_bwd;  /* [num_kblocks_bwd][16] */
 } ffa_block_meta_view_t;
 
 /* Upper bound on the metadata buffer size for a table of num_slices slices.

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol():
 
 def test_abi_version_and_strings():
     L = ffa.lib()
-    assert L.ffa_abi_version() == 5
+    assert L.ffa_abi_version() == 6
     for code in range(7):
         assert len(L.ffa_status_string(code)) > 0
     assert L.ffa_status_string(99) == b"unknown status"

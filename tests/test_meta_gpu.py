@@ -53,7 +53,30 @@ def check_meta(slices, Tq, Tk, d=128, meta=None):
         mo = csr[which]["mask_block_offset"].numpy()
         cost = 4 * np.diff(fo) + 5 * np.diff(mo)
         assert np.all(np.diff(cost[s]) <= 0)
+        check_records(csr, which, s, fo, mo)
     return m, csr
+
+
+def check_records(csr, which, s, fo, mo):
+    """Block records in schedule order: owner, list offsets and counts, and the
+    first (q2k) or last (k2q) entry of each list, -1 for an empty list."""
+    rec = csr["records_fwd" if which == "q2k" else "records_bwd"].numpy()
+    fi = csr[which]["full_block_idx"].numpy()
+    mi = csr[which]["mask_block_idx"].numpy()
+    nf, nm = fo[s + 1] - fo[s], mo[s + 1] - mo[s]
+    assert np.array_equal(rec[:, 0], s)
+    assert np.array_equal(rec[:, 1], fo[s]) and np.array_equal(rec[:, 2], nf)
+    assert np.array_equal(rec[:, 3], mo[s]) and np.array_equal(rec[:, 4], nm)
+    if which == "q2k":
+        qs = csr["qblock_slice_offset"].numpy()
+        assert np.array_equal(rec[:, 5], qs[s]) and np.array_equal(rec[:, 6], qs[s + 1] - qs[s])
+        tf = np.where(nf > 0, fi[np.minimum(fo[s], max(len(fi) - 1, 0))] if len(fi) else -1, -1)
+        tp = np.where(nm > 0, mi[np.minimum(mo[s], max(len(mi) - 1, 0))] if len(mi) else -1, -1)
+        assert np.array_equal(rec[:, 7], tf) and np.array_equal(rec[:, 8], tp)
+    else:
+        tf = np.where(nf > 0, fi[np.clip(fo[s] + nf - 1, 0, max(len(fi) - 1, 0))] if len(fi) else -1, -1)
+        tp = np.where(nm > 0, mi[np.clip(mo[s] + nm - 1, 0, max(len(mi) - 1, 0))] if len(mi) else -1, -1)
+        assert np.array_equal(rec[:, 5], tf) and np.array_equal(rec[:, 6], tp)
 
 
 @pytest.mark.parametrize("variant", ["causal", "mixed", "two_full"])
