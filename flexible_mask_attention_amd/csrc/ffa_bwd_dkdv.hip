@@ -10,9 +10,11 @@
 //   dP = dO V^T, dS = P (dP - D), dK += dS^T Q.
 // Each lane owns one key (S = Q K^T leaves keys on lanes), so P and dS feed the
 // dV^T / dK^T MFMAs as B operands and dO^T, Q^T come from LDS through
-// transposed reads.  This file is compiled on its own so that it can use the
-// memory-clause scheduling strategy, which measured faster for this kernel
-// (the dQ kernel spills with it).
+// transposed reads.  At head_dim 128 each half's two MFMA phases (S / dP, then
+// dV / dK) are inline-assembly blocks that read their LDS operands through a
+// ring of registers several MFMAs ahead of use.  This file is compiled on its
+// own so that it can use the memory-clause scheduling strategy, which
+// measured faster for this kernel (the dQ kernel spills with it).
 #include <type_traits>
 
 #include "ffa_internal.hpp"
@@ -22,6 +24,122 @@ namespace ffa {
 namespace {
 
 constexpr int NT = 256;
+
+// dV^T += dO^T P and dK^T += Q^T dS of one 32-row half at head_dim 128: 16
+// MFMAs (16-row chunk c2, column block mb, dV then dK) whose A operands are
+// pairs of transposed 64-bit LDS reads.  A ring of four 4-register operand
+// buffers in fixed registers, v240-v255 (an operand's two 64-bit halves
+// cannot be named separately in inline assembly), keeps each MFMA's reads
+// three MFMAs ahead of it instead of just before it (the compiler's own
+// schedule, register bound at two waves per SIMD).  Same MFMAs in the same
+// order as the plain loop, so the sums are bitwise identical.  The block
+// waits for its own LDS reads (a wait for at most N outstanding also covers
+// older LDS or scalar loads).  A buffer is refilled right after the MFMA that
+// read it: an MFMA reads its A / B operands when it is issued, and the
+// compiler schedules the same pattern.  The first MFMA follows eight LDS
+// instructions, more than the wait states a VALU write of its B operand
+// needs.
+#define FFA_TR2(lo, hi, off) \
+  "ds_read_b64_tr_b16 v[" lo "], %12 offset:(%14+" #off ")\n\t" \
+  "ds_read_b64_tr_b16 v[" hi "], %13 offset:(%14+" #off ")\n\t"
+#define FFA_B0 "240:241", "242:243"
+#define FFA_B1 "244:245", "246:247"
+#define FFA_B2 "248:249", "250:251"
+#define FFA_B3 "252:253", "254:255"
+#define FFA_Q0 "v[240:243]"
+#define FFA_Q1 "v[244:247]"
+#define FFA_Q2 "v[248:251]"
+#define FFA_Q3 "v[252:255]"
+#define FFA_RDX(b, off) FFA_TR2(b, off)
+#define FFA_M(acc, buf, bop) "v_mfma_f32_32x32x16_bf16 " acc ", " buf ", " bop ", " acc "\n\t"
+#define FFA_W(n) "s_waitcnt lgkmcnt(" #n ")\n\t"
+// operands: %0-%3 dV^T column blocks, %4-%7 dK^T column blocks, %8 / %9 P /
+// dS of chunk 0, %10 / %11 of chunk 1, %12 / %13 transposed-read addresses of
+// rows 0-7 / 8-15, %14 LDS offset of the stage and half.  Read offsets: dO^T
+// at 16384 + 4096 mb + 1024 c2, Q^T at 4096 mb + 1024 c2.
+#define FFA_DKDV_BLOCK \
+  FFA_RDX(FFA_B0, 16384) FFA_RDX(FFA_B1, 0) FFA_RDX(FFA_B2, 20480) FFA_RDX(FFA_B3, 4096) \
+  FFA_W(6) FFA_M("%0", FFA_Q0, "%8") FFA_RDX(FFA_B0, 24576) \
+  FFA_W(6) FFA_M("%4", FFA_Q1, "%9") FFA_RDX(FFA_B1, 8192) \
+  FFA_W(6) FFA_M("%1", FFA_Q2, "%8") FFA_RDX(FFA_B2, 28672) \
+  FFA_W(6) FFA_M("%5", FFA_Q3, "%9") FFA_RDX(FFA_B3, 12288) \
+  FFA_W(6) FFA_M("%2", FFA_Q0, "%8") FFA_RDX(FFA_B0, 17408) \
+  FFA_W(6) FFA_M("%6", FFA_Q1, "%9") FFA_RDX(FFA_B1, 1024) \
+  FFA_W(6) FFA_M("%3", FFA_Q2, "%8") FFA_RDX(FFA_B2, 21504) \
+  FFA_W(6) FFA_M("%7", FFA_Q3, "%9") FFA_RDX(FFA_B3, 5120) \
+  FFA_W(6) FFA_M("%0", FFA_Q0, "%10") FFA_RDX(FFA_B0, 25600) \
+  FFA_W(6) FFA_M("%4", FFA_Q1, "%11") FFA_RDX(FFA_B1, 9216) \
+  FFA_W(6) FFA_M("%1", FFA_Q2, "%10") FFA_RDX(FFA_B2, 29696) \
+  FFA_W(6) FFA_M("%5", FFA_Q3, "%11") FFA_RDX(FFA_B3, 13312) \
+  FFA_W(6) FFA_M("%2", FFA_Q0, "%10") \
+  FFA_W(4) FFA_M("%6", FFA_Q1, "%11") \
+  FFA_W(2) FFA_M("%3", FFA_Q2, "%10") \
+  FFA_W(0) FFA_M("%7", FFA_Q3, "%11")
+
+template <int BASE>
+__device__ __forceinline__ void dkdv_half_d128(f32x16 (&dv)[4], f32x16 (&dk)[4], const bf16x8& p0,
+                                               const bf16x8& s0, const bf16x8& p1, const bf16x8& s1,
+                                               int t0, int t1) {
+  asm volatile(FFA_DKDV_BLOCK
+               : "+v"(dv[0]), "+v"(dv[1]), "+v"(dv[2]), "+v"(dv[3]), "+v"(dk[0]), "+v"(dk[1]),
+                 "+v"(dk[2]), "+v"(dk[3])
+               : "v"(p0), "v"(s0), "v"(p1), "v"(s1), "v"(t0), "v"(t1), "i"(BASE)
+               : "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250",
+                 "v251", "v252", "v253", "v254", "v255", "memory");
+}
+
+// S - LSE / scale = Q K^T - LSE / scale and dP - D = dO V^T - D of one
+// 32-row half at head_dim 128 (lane = key, register r = row 8(r/4) + 4 h32 +
+// r%4 of the half).  The accumulators are fixed registers, v208-v223 (S) and
+// v224-v239 (dP), so that the block itself can load the row statistics into
+// their 4-register groups (an operand's parts cannot be named separately in
+// inline assembly); the 16 Q / dO operand reads go through a ring of four
+// 128-bit buffers (v240-v255, shared with the dV / dK block) three MFMAs
+// ahead of their use.  Same MFMAs in the same order as the plain loop (the S
+// and dP chains interleaved), so the sums are bitwise identical.  The block
+// ends with 16 wait states, more than a VALU read of an MFMA result needs.
+#define FFA_RS(regs, off) "ds_read_b128 v[" regs "], %20 offset:(%22+" #off ")\n\t"
+#define FFA_RQ(regs, addr, off) "ds_read_b128 v[" regs "], " addr " offset:(%21+" #off ")\n\t"
+// operands: %0 S, %1 dP, %2-%9 K and %10-%17 V operands of the eight 16-wide
+// d steps, %18 / %19 Q / dO read address of column pair 0 / 1, %20 row
+// statistics address, %21 / %22 LDS offset of the stage and half for the
+// operand / statistics reads.  Q at 4096 (k / 2), dO 16384 further; LSE
+// terms at 32 j, D terms 256 further.
+#define FFA_SDP_KV_BLOCK \
+  FFA_RS("208:211", 0) FFA_RS("212:215", 32) FFA_RS("216:219", 64) FFA_RS("220:223", 96) \
+  FFA_RS("224:227", 256) FFA_RS("228:231", 288) FFA_RS("232:235", 320) FFA_RS("236:239", 352) \
+  FFA_RQ("240:243", "%18", 0) FFA_RQ("244:247", "%18", 16384) \
+  FFA_RQ("248:251", "%19", 0) FFA_RQ("252:255", "%19", 16384) \
+  FFA_W(3) FFA_M("v[208:223]", "v[240:243]", "%2") FFA_RQ("240:243", "%18", 4096) \
+  FFA_W(3) FFA_M("v[224:239]", "v[244:247]", "%10") FFA_RQ("244:247", "%18", 20480) \
+  FFA_W(3) FFA_M("v[208:223]", "v[248:251]", "%3") FFA_RQ("248:251", "%19", 4096) \
+  FFA_W(3) FFA_M("v[224:239]", "v[252:255]", "%11") FFA_RQ("252:255", "%19", 20480) \
+  FFA_W(3) FFA_M("v[208:223]", "v[240:243]", "%4") FFA_RQ("240:243", "%18", 8192) \
+  FFA_W(3) FFA_M("v[224:239]", "v[244:247]", "%12") FFA_RQ("244:247", "%18", 24576) \
+  FFA_W(3) FFA_M("v[208:223]", "v[248:251]", "%5") FFA_RQ("248:251", "%19", 8192) \
+  FFA_W(3) FFA_M("v[224:239]", "v[252:255]", "%13") FFA_RQ("252:255", "%19", 24576) \
+  FFA_W(3) FFA_M("v[208:223]", "v[240:243]", "%6") FFA_RQ("240:243", "%18", 12288) \
+  FFA_W(3) FFA_M("v[224:239]", "v[244:247]", "%14") FFA_RQ("244:247", "%18", 28672) \
+  FFA_W(3) FFA_M("v[208:223]", "v[248:251]", "%7") FFA_RQ("248:251", "%19", 12288) \
+  FFA_W(3) FFA_M("v[224:239]", "v[252:255]", "%15") FFA_RQ("252:255", "%19", 28672) \
+  FFA_W(3) FFA_M("v[208:223]", "v[240:243]", "%8") \
+  FFA_W(2) FFA_M("v[224:239]", "v[244:247]", "%16") \
+  FFA_W(1) FFA_M("v[208:223]", "v[248:251]", "%9") \
+  FFA_W(0) FFA_M("v[224:239]", "v[252:255]", "%17") \
+  "s_nop 7\n\ts_nop 7"
+
+template <int BASE_T, int BASE_L>
+__device__ __forceinline__ void sdp_kv_d128(f32x16& s, f32x16& p, const bf16x8 (&k)[8],
+                                            const bf16x8 (&v)[8], int r0, int r1, int la) {
+  asm volatile(FFA_SDP_KV_BLOCK
+               : "={v[208:223]}"(s), "={v[224:239]}"(p)
+               : "v"(k[0]), "v"(k[1]), "v"(k[2]), "v"(k[3]), "v"(k[4]), "v"(k[5]), "v"(k[6]),
+                 "v"(k[7]), "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]),
+                 "v"(v[6]), "v"(v[7]),
+                 "v"(r0), "v"(r1), "v"(la), "i"(BASE_T), "i"(BASE_L)
+               : "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250",
+                 "v251", "v252", "v253", "v254", "v255", "memory");
+}
 
 // ---------------------------------------------------------------------------
 // dK, dV: owner (kv head, BN_B-key block), 4 waves x 32 keys.
@@ -139,6 +257,13 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   for (int j = 0; j < 2; ++j)
     taddr[j] = lds_pos(4 * h32 + (t16 >> 2) + 8 * j, 2 * (g16 & 1) + ((t16 >> 1) & 1)) + 8 * (t16 & 1);
   const int laddr = 2 * TILE_B + 16 * h32;   // row-stat reads: + (32qb + 8j) * 4
+  // LDS byte addresses for the inline blocks at d = 128: operand reads of
+  // column pair 0 / 1, transposed reads of rows 0-7 / 8-15 of a chunk, and
+  // the row statistics
+  const uint32_t smem_base = (uint32_t)(size_t)((__attribute__((address_space(3))) char*)smem);
+  const int rb0 = (int)(smem_base + raddr[0]), rb1 = (int)(smem_base + raddr[1]);
+  const int tb0 = (int)(smem_base + taddr[0]), tb1 = (int)(smem_base + taddr[1]);
+  const int lb0 = (int)(smem_base + laddr);
 
   f32x16 dkacc[MB], dvacc[MB];
 #pragma unroll
@@ -163,11 +288,11 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     // Partial tile: valid rows of this key inside [m0, m0 + BM_B) from the
     // slices of the enclosing forward query block, one bit per row.  A half
     // with no valid pair for any of the wave's keys is skipped.
-    uint64_t mk = 0, mkf = 0;
     if (masked) {
       // the query heads of one tile come one after the other and share its
       // mask: it is built at the first of them and kept for the rest
       if (m != mask_tile) {
+        uint64_t mkf = 0;
         const int m0 = m * BM_B;
         const int mf = m0 / BM_F;
         const int s0 = mv.qs_off[mf], nS = mv.qs_off[mf + 1] - s0;
@@ -182,45 +307,47 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         }
         mask_tile = m;
         mask_keep = mkf;
-      } else {
-        mkf = mask_keep;
       }
-      mk = mkf >> (4 * h32);
     }
 
     // one 32-row half at a time, so that only one S / dP pair is live
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      if (masked && __ballot(((mkf >> (32 * qb)) & 0xffffffffull) != 0) == 0) continue;
+      if (masked && __ballot(((mask_keep >> (32 * qb)) & 0xffffffffull) != 0) == 0) continue;
       // S - LSE / scale = Q K^T - LSE / scale and dP - D = dO V^T - D; lane =
       // key, registers = rows 32qb + 8(r/4) + 4*h32 + r%4.  Both accumulators
       // start at their row statistic (four 128-bit LDS reads each, issued
       // before the MFMAs): P = exp2(c (S - LSE / scale)) = exp2(S c - LSE
       // log2 e) then needs one multiply, and dS = P (dP - D) no subtraction.
       f32x16 sacc, pacc;
+      if constexpr (D == 128) {
+        if (qb == 0) sdp_kv_d128<stage * STAGE_B, stage * STAGE_B>(sacc, pacc, kop, vop, rb0, rb1, lb0);
+        else sdp_kv_d128<stage * STAGE_B + 32 * 64, stage * STAGE_B + 32 * 4>(sacc, pacc, kop, vop, rb0, rb1, lb0);
+      } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 nd = *(const __attribute__((address_space(3))) f32x4*)(
-            lb + laddr + (32 * qb + 8 * j) * 4 + BM_B * 4);
-        const f32x4 nm = *(const __attribute__((address_space(3))) f32x4*)(lb + laddr + (32 * qb + 8 * j) * 4);
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 nd = *(const __attribute__((address_space(3))) f32x4*)(
+              lb + laddr + (32 * qb + 8 * j) * 4 + BM_B * 4);
+          const f32x4 nm = *(const __attribute__((address_space(3))) f32x4*)(lb + laddr + (32 * qb + 8 * j) * 4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pacc[4 * j + i] = nd[i];
-          sacc[4 * j + i] = nm[i];
+          for (int i = 0; i < 4; ++i) {
+            pacc[4 * j + i] = nd[i];
+            sacc[4 * j + i] = nm[i];
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+          bf16x8 qa, ga;
+          u32x4 u1 = *(const __attribute__((address_space(3))) u32x4*)(lb + (k >> 1) * GB + raddr[k & 1] + qb * 32 * 64);
+          u32x4 u2 = *(const __attribute__((address_space(3))) u32x4*)(lb + TILE_B + (k >> 1) * GB + raddr[k & 1] + qb * 32 * 64);
+          __builtin_memcpy(&qa, &u1, 16);
+          __builtin_memcpy(&ga, &u2, 16);
+          sacc = mfma32(qa, kop[k], sacc);
+          pacc = mfma32(ga, vop[k], pacc);
         }
       }
-#pragma unroll
-      for (int k = 0; k < KS; ++k) {
-        bf16x8 qa, ga;
-        u32x4 u1 = *(const __attribute__((address_space(3))) u32x4*)(lb + (k >> 1) * GB + raddr[k & 1] + qb * 32 * 64);
-        u32x4 u2 = *(const __attribute__((address_space(3))) u32x4*)(lb + TILE_B + (k >> 1) * GB + raddr[k & 1] + qb * 32 * 64);
-        __builtin_memcpy(&qa, &u1, 16);
-        __builtin_memcpy(&ga, &u2, 16);
-        sacc = mfma32(qa, kop[k], sacc);
-        pacc = mfma32(ga, vop[k], pacc);
-      }
       if (masked) {
-        const uint32_t w = static_cast<uint32_t>(mk >> (32 * qb));
+        const uint32_t w = static_cast<uint32_t>((mask_keep >> (4 * h32)) >> (32 * qb));
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           sacc[r] = keep_or_neg_inf(sacc[r], w, 8 * (r >> 2) + (r & 3));
@@ -235,6 +362,20 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
       }
 
       // dV^T += dO^T P and dK^T += Q^T dS over the half's two 16-row chunks
+      if constexpr (D == 128) {
+        static_assert(TILE_B == 16384 && GB == 4096 && MB == 4, "offsets of the d = 128 block");
+        bf16x8 pb[2], sb[2];
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            pb[c2][e] = static_cast<__bf16>(sacc[8 * c2 + e]);
+            sb[c2][e] = static_cast<__bf16>(pacc[8 * c2 + e]);
+          }
+        static_assert(QB == 2, "two halves per tile");
+        if (qb == 0) dkdv_half_d128<stage * STAGE_B>(dvacc, dkacc, pb[0], sb[0], pb[1], sb[1], tb0, tb1);
+        else dkdv_half_d128<stage * STAGE_B + 32 * 64>(dvacc, dkacc, pb[0], sb[0], pb[1], sb[1], tb0, tb1);
+      } else
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
         bf16x8 pb, sb;
@@ -270,6 +411,13 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     tile(std::integral_constant<int, 0>{}, u);
     if (u + 1 < uend) tile(std::integral_constant<int, 1>{}, u + 1);
   }
+
+  // the last MFMAs of the inline block wrote the accumulators; give them the
+  // wait states a VALU or memory read of an MFMA result needs
+  if constexpr (D == 128)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3"
+                 : "+v"(dvacc[0]), "+v"(dvacc[1]), "+v"(dvacc[2]), "+v"(dvacc[3]), "+v"(dkacc[0]),
+                   "+v"(dkacc[1]), "+v"(dkacc[2]), "+v"(dkacc[3]));
 
   if (part >= 0) {
     // Both halves store their fp32 partial sums, then count themselves in;
