@@ -129,6 +129,44 @@ __device__ __forceinline__ void sdp_d128(f32x16& sacc, f32x16& pacc, const bf16x
 #undef FFA_SDP_OPS
 }
 
+// dQ^T += K^T dS^T of one 32-key stage at head_dim 128: 8 MFMAs (16-key
+// chunk c, column block mb) whose A operands are pairs of transposed 64-bit
+// LDS reads, through a ring of three 4-register operand buffers in fixed
+// registers, v156-v167 (an operand's two 64-bit halves cannot be named
+// separately in inline assembly).  Same MFMAs in the same order as the plain
+// loop (bitwise identical sums); the same waits and refill rule as the S / dP
+// block above.  The first MFMA follows LDS instructions enough for the wait
+// states a VALU write of its B operand needs.
+#define FFA_OTR(lo, hi, off) \
+  "ds_read_b64_tr_b16 v[" lo "], %6 offset:(%8+" #off ")\n\t" \
+  "ds_read_b64_tr_b16 v[" hi "], %7 offset:(%8+" #off ")\n\t"
+#define FFA_M(acc, buf, bop) "v_mfma_f32_32x32x16_bf16 " acc ", " buf ", " bop ", " acc "\n\t"
+#define FFA_W(n) "s_waitcnt lgkmcnt(" #n ")\n\t"
+// operands: %0-%3 dQ^T column blocks, %4 / %5 dS^T of chunk 0 / 1, %6 / %7
+// transposed-read addresses of keys 0-7 / 8-15 of a chunk, %8 LDS offset of
+// the stage's K tile.  Read offsets 2048 mb + 1024 c.
+#define FFA_DQ_BLOCK \
+  FFA_OTR("156:157", "158:159", 0) FFA_OTR("160:161", "162:163", 2048) \
+  FFA_OTR("164:165", "166:167", 4096) \
+  FFA_W(4) FFA_M("%0", "v[156:159]", "%4") FFA_OTR("156:157", "158:159", 6144) \
+  FFA_W(4) FFA_M("%1", "v[160:163]", "%4") FFA_OTR("160:161", "162:163", 1024) \
+  FFA_W(4) FFA_M("%2", "v[164:167]", "%4") FFA_OTR("164:165", "166:167", 3072) \
+  FFA_W(4) FFA_M("%3", "v[156:159]", "%4") FFA_OTR("156:157", "158:159", 5120) \
+  FFA_W(4) FFA_M("%0", "v[160:163]", "%5") FFA_OTR("160:161", "162:163", 7168) \
+  FFA_W(4) FFA_M("%1", "v[164:167]", "%5") \
+  FFA_W(2) FFA_M("%2", "v[156:159]", "%5") \
+  FFA_W(0) FFA_M("%3", "v[160:163]", "%5")
+
+template <int BASE>
+__device__ __forceinline__ void dq_d128(f32x16 (&o)[4], const bf16x8& p0, const bf16x8& p1, int t0,
+                                        int t1) {
+  asm volatile(FFA_DQ_BLOCK
+               : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3])
+               : "v"(p0), "v"(p1), "v"(t0), "v"(t1), "i"(BASE)
+               : "v156", "v157", "v158", "v159", "v160", "v161", "v162", "v163", "v164", "v165",
+                 "v166", "v167", "memory");
+}
+
 // PRE: also compute this block's -D and LSE log2 e rows (the bwd_pre work)
 // from the dO operand already in registers and O, use them, and store them
 // for the dK/dV kernel, which then runs after this one.
@@ -244,6 +282,8 @@ __global__ __launch_bounds__(NT, 3) __attribute__((amdgpu_waves_per_eu(3, 3))) v
 #pragma unroll
   for (int j = 0; j < 2; ++j)
     taddr[j] = lds_pos(4 * h32 + (t16 >> 2) + 8 * j, 2 * (g16 & 1) + ((t16 >> 1) & 1)) + 8 * (t16 & 1);
+  // LDS byte addresses of the transposed K reads for the dQ block at d = 128
+  const int tb0 = (int)(smem_base + taddr[0]), tb1 = (int)(smem_base + taddr[1]);
 
   // waves 0-1 load the K stage tile, waves 2-3 the V stage tile
   TileDma<D, SK> dm;
@@ -331,6 +371,15 @@ __global__ __launch_bounds__(NT, 3) __attribute__((amdgpu_waves_per_eu(3, 3))) v
       }
 
       // dQ^T += K^T dS^T over the stage's two 16-key chunks
+      if constexpr (D == 128) {
+        static_assert(GB == 2048 && MB == 4 && SK == 32, "offsets of the d = 128 block");
+        bf16x8 sb[2];
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sb[c2][e] = static_cast<__bf16>(pacc[8 * c2 + e]);
+        dq_d128<stage * STAGE_B>(dqacc, sb[0], sb[1], tb0, tb1);
+      } else
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
         bf16x8 sb;
@@ -359,6 +408,12 @@ __global__ __launch_bounds__(NT, 3) __attribute__((amdgpu_waves_per_eu(3, 3))) v
     stage_fn(std::integral_constant<int, 0>{}, u);
     if (u + 1 < nU) stage_fn(std::integral_constant<int, 1>{}, u + 1);
   }
+
+  // the last MFMAs of the inline block wrote dQ^T; give them the wait states
+  // a VALU or memory read of an MFMA result needs
+  if constexpr (D == 128)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3"
+                 : "+v"(dqacc[0]), "+v"(dqacc[1]), "+v"(dqacc[2]), "+v"(dqacc[3]));
 
   if ((a.flags & FFA_ACCUMULATE) == 0) {
     // Plain store, staged through the idle tile ring so that each global
