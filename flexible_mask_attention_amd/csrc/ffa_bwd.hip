@@ -373,6 +373,7 @@ __global__ __launch_bounds__(NT, 3) __attribute__((amdgpu_waves_per_eu(3, 3))) v
       // dQ^T += K^T dS^T over the stage's two 16-key chunks
       if constexpr (D == 128) {
         static_assert(GB == 2048 && MB == 4 && SK == 32, "offsets of the d = 128 block");
+        static_assert(STAGE_B + 3 * GB + 1024 < 65536, "LDS read offsets of the d = 128 block");
         bf16x8 sb[2];
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2)

@@ -363,7 +363,12 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
 
       // dV^T += dO^T P and dK^T += Q^T dS over the half's two 16-row chunks
       if constexpr (D == 128) {
-        static_assert(TILE_B == 16384 && GB == 4096 && MB == 4, "offsets of the d = 128 block");
+        static_assert(TILE_B == 16384 && GB == 4096 && MB == 4, "offsets of the d = 128 blocks");
+        // the largest LDS offset either block encodes must fit the 16-bit field
+        // (the row statistics' 2 TILE_B is in their address register)
+        static_assert(STAGE_B + 32 * 64 + TILE_B + 3 * GB + 1024 < 65536 &&
+                          STAGE_B + 32 * 4 + 3 * 32 + BM_B * 4 < 65536,
+                      "LDS read offsets of the d = 128 blocks");
         bf16x8 pb[2], sb[2];
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2)
