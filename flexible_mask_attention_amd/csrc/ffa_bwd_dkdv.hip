@@ -93,9 +93,10 @@ __device__ __forceinline__ void dkdv_half_d128(f32x16 (&dv)[4], f32x16 (&dk)[4],
 // r%4 of the half).  The accumulators are fixed registers, v208-v223 (S) and
 // v224-v239 (dP), so that the block itself can load the row statistics into
 // their 4-register groups (an operand's parts cannot be named separately in
-// inline assembly); the 16 Q / dO operand reads go through a ring of four
-// 128-bit buffers (v240-v255, shared with the dV / dK block) three MFMAs
-// ahead of their use.  Same MFMAs in the same order as the plain loop (the S
+// inline assembly); they are early-clobber outputs, as the block writes them
+// before it has read its inputs.  The 16 Q / dO operand reads go through a
+// ring of four 128-bit buffers (v240-v255, shared with the dV / dK block)
+// three MFMAs ahead of their use.  Same MFMAs in the same order as the plain loop (the S
 // and dP chains interleaved), so the sums are bitwise identical.  The block
 // ends with 16 wait states, more than a VALU read of an MFMA result needs.
 #define FFA_RS(regs, off) "ds_read_b128 v[" regs "], %20 offset:(%22+" #off ")\n\t"
@@ -132,7 +133,7 @@ template <int BASE_T, int BASE_L>
 __device__ __forceinline__ void sdp_kv_d128(f32x16& s, f32x16& p, const bf16x8 (&k)[8],
                                             const bf16x8 (&v)[8], int r0, int r1, int la) {
   asm volatile(FFA_SDP_KV_BLOCK
-               : "={v[208:223]}"(s), "={v[224:239]}"(p)
+               : "=&{v[208:223]}"(s), "=&{v[224:239]}"(p)
                : "v"(k[0]), "v"(k[1]), "v"(k[2]), "v"(k[3]), "v"(k[4]), "v"(k[5]), "v"(k[6]),
                  "v"(k[7]), "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]),
                  "v"(v[6]), "v"(v[7]),
