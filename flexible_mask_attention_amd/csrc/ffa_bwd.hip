@@ -77,25 +77,33 @@ constexpr size_t dq_lds_bytes() {
   return 2 * 2 * DQ_SK * D * 2 + (size_t)(NT / 64) * dq_nql<D>() * 1024;
 }
 
-// S^T = K Q^T and dP^T = V dO^T of one 32-key stage at head_dim 128 (the
-// first three 16-wide d steps of Q in registers, the last five parked in LDS),
-// as one block with a ring of three 128-bit operand buffers: each MFMA's LDS
-// operand is read two to three reads ahead of its use instead of just before
-// it (the compiler's own schedule, register-bound at three waves per SIMD).  Same MFMAs in the same
-// order as the plain loop (bitwise identical sums).  The buffers and
-// accumulators are outputs, so the compiler keeps nothing else in them; the
-// block waits for its own LDS reads (a wait for at most N outstanding also
-// covers any older LDS or scalar loads) and ends with 16 wait states, more
-// than an 8-pass MFMA result needs before a VALU instruction may read it.
+// S^T = K Q^T and dP^T - D = V dO^T - D of one 32-key stage at head_dim 128
+// (the first three 16-wide d steps of Q in registers, the last five parked in
+// LDS), as one block with a ring of three 128-bit operand buffers: each
+// MFMA's LDS operand is read two to three reads ahead of its use instead of
+// just before it (the compiler's own schedule, register-bound at three waves
+// per SIMD).  The dP^T accumulator sits in fixed registers, v140-v155, so that
+// the block can seed all 16 with -D (eight 64-bit moves of the (-D, -D) pair,
+// seven instructions before the first dP MFMA reads them); dS = P (dP - D)
+// then needs one multiply.  The S MFMAs are the plain loop's, in its order.
+// The buffers and accumulators are early-clobber outputs, so the compiler
+// keeps nothing else in them; the block waits for its own LDS reads (a wait
+// for at most N outstanding also covers any older LDS or scalar loads) and
+// ends with 16 wait states, more than an 8-pass MFMA result needs before a
+// VALU instruction may read it.
 #define FFA_RD(buf, addr, off) "ds_read_b128 " buf ", " addr " offset:" #off "\n\t"
 #define FFA_MF(d, a, b, c) "v_mfma_f32_32x32x16_bf16 " d ", " a ", " b ", " c "\n\t"
 #define FFA_WT(n) "s_waitcnt lgkmcnt(" #n ")\n\t"
-// operands: %0 S, %1 dP, %2-%4 buffers, %5-%7 Q chunks 0-2, %8-%15 dO chunks
-// 0-7, %16 / %17 K/V read address of column pair 0 / 1, %18 parked Q chunks 3-7
+// operands: %0 S, %1 dP (v140-v155), %2-%4 buffers, %5-%7 Q chunks 0-2,
+// %8-%15 dO chunks 0-7, %16 / %17 K/V read address of column pair 0 / 1, %18
+// parked Q chunks 3-7, %19 the (-D, -D) pair
 #define FFA_SDP_BLOCK(K0, K1, K2, K3, V0, V1, V2, V3) \
+  "v_mov_b64 v[140:141], %19\n\tv_mov_b64 v[142:143], %19\n\tv_mov_b64 v[144:145], %19\n\t" \
+  "v_mov_b64 v[146:147], %19\n\tv_mov_b64 v[148:149], %19\n\tv_mov_b64 v[150:151], %19\n\t" \
+  "v_mov_b64 v[152:153], %19\n\tv_mov_b64 v[154:155], %19\n\t" \
   FFA_RD("%2", "%16", K0) FFA_RD("%3", "%16", V0) FFA_RD("%4", "%17", K0) \
   FFA_WT(2) FFA_MF("%0", "%2", "%5", "0") FFA_RD("%2", "%17", V0) \
-  FFA_WT(2) FFA_MF("%1", "%3", "%8", "0") FFA_RD("%3", "%16", K1) \
+  FFA_WT(2) FFA_MF("%1", "%3", "%8", "%1") FFA_RD("%3", "%16", K1) \
   FFA_WT(2) FFA_MF("%0", "%4", "%6", "%0") FFA_RD("%4", "%16", V1) \
   FFA_WT(2) FFA_MF("%1", "%2", "%9", "%1") FFA_RD("%2", "%17", K1) \
   FFA_WT(2) FFA_MF("%0", "%3", "%7", "%0") FFA_RD("%3", "%18", 0) \
@@ -115,12 +123,12 @@ constexpr size_t dq_lds_bytes() {
 template <int STAGE>
 __device__ __forceinline__ void sdp_d128(f32x16& sacc, f32x16& pacc, const bf16x8 (&q)[8],
                                          const bf16x8 (&g)[8], uint32_t k0, uint32_t k1,
-                                         uint32_t qp) {
+                                         uint32_t qp, uint64_t nd2) {
   u32x4 b0, b1, b2;
 #define FFA_SDP_OPS                                                                         \
-  : "=&v"(sacc), "=&v"(pacc), "=&v"(b0), "=&v"(b1), "=&v"(b2)                              \
+  : "=&v"(sacc), "=&{v[140:155]}"(pacc), "=&v"(b0), "=&v"(b1), "=&v"(b2)                   \
   : "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(g[0]), "v"(g[1]), "v"(g[2]), "v"(g[3]), \
-    "v"(g[4]), "v"(g[5]), "v"(g[6]), "v"(g[7]), "v"(k0), "v"(k1), "v"(qp)                 \
+    "v"(g[4]), "v"(g[5]), "v"(g[6]), "v"(g[7]), "v"(k0), "v"(k1), "v"(qp), "v"(nd2)      \
   : "memory"
   if constexpr (STAGE == 0)
     asm volatile(FFA_SDP_BLOCK(0, 2048, 4096, 6144, 8192, 10240, 12288, 14336) FFA_SDP_OPS);
@@ -262,6 +270,8 @@ __global__ __launch_bounds__(NT, 3) __attribute__((amdgpu_waves_per_eu(3, 3))) v
     }
   }
   wait_vmem();
+  // (-D, -D) as one 64-bit operand: the dP^T accumulator's seed
+  const uint64_t nd2 = ((uint64_t)__float_as_uint(ndval) << 32) | __float_as_uint(ndval);
   char* qlds = smem + 2 * STAGE_B + wid * (NQL * 1024) + lane * 16;
 #pragma unroll
   for (int k = QREG; k < KS; ++k) {
@@ -336,7 +346,7 @@ __global__ __launch_bounds__(NT, 3) __attribute__((amdgpu_waves_per_eu(3, 3))) v
       // S^T = K Q^T and dP^T = V dO^T; lane = query row, registers = keys 8(r/4) + 4*h32 + r%4
       f32x16 sacc, pacc;
       if constexpr (D == 128 && NQL == 5) {
-        sdp_d128<stage>(sacc, pacc, qop, gop, kbase0, kbase1, qbase);
+        sdp_d128<stage>(sacc, pacc, qop, gop, kbase0, kbase1, qbase, nd2);
       } else {
         sacc = f32x16{};
         pacc = f32x16{};
@@ -367,7 +377,8 @@ __global__ __launch_bounds__(NT, 3) __attribute__((amdgpu_waves_per_eu(3, 3))) v
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -l2));
-        pacc[r] = pv * (pacc[r] + ndval);
+        if constexpr (D == 128 && NQL == 5) pacc[r] *= pv;   // the block seeded it with -D
+        else pacc[r] = pv * (pacc[r] + ndval);
       }
 
       // dQ^T += K^T dS^T over the stage's two 16-key chunks
