@@ -195,7 +195,7 @@ void ffa_fwd_kernel(FwdArgs a) {
           sacc[r] = keep_or_neg_inf(sacc[r], w, 8 * (r >> 2) + (r & 3));
       }
       bf16x8 pop[2];
-      float psum = 0.f;
+      float psum;
       bool exact = !all_finite;
       if (!exact) {
         // P against the stored max; the scores stay in sacc for the exact path
@@ -203,7 +203,7 @@ void ffa_fwd_kernel(FwdArgs a) {
         for (int r = 0; r < 16; ++r) {
           const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -mc));
           pop[r >> 3][r & 7] = static_cast<__bf16>(pv);
-          psum += pv;
+          psum = r == 0 ? pv : psum + pv;   // no 0 + first term
         }
         exact = __ballot(!(psum <= PSUM_LIMIT)) != 0;
       }
@@ -226,12 +226,11 @@ void ffa_fwd_kernel(FwdArgs a) {
         }
         mc = (m_run == -INFINITY) ? 0.f : m_run * c;
         all_finite = __ballot(m_run == -INFINITY) == 0;
-        psum = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -mc));
           pop[r >> 3][r & 7] = static_cast<__bf16>(pv);
-          psum += pv;
+          psum = r == 0 ? pv : psum + pv;
         }
       }
       l_run += psum;
