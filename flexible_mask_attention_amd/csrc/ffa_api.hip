@@ -46,6 +46,25 @@ bool check_tensor(const void* p, int64_t ts, int64_t hs, int64_t T, int64_t H, i
   return true;
 }
 
+// An output's rows (one per token and head, head_dim elements each) must not
+// share elements, or two workgroups would race on them: with the axes of
+// more than one element ordered by stride, the inner stride must be at
+// least head_dim and the outer one must clear all rows of the inner axis.
+// Views into one packed tensor (say dq, dk, dv of [T][3 H][D]) pass.
+bool rows_disjoint(int64_t ts, int64_t hs, int64_t T, int64_t H, int D) {
+  if (T == 0) return true;
+  int64_t s_in = ts, n_in = T, s_out = hs, n_out = H;
+  if (n_in == 1 || (n_out > 1 && hs < ts)) {
+    s_in = hs;
+    n_in = H;
+    s_out = ts;
+    n_out = T;
+  }
+  if (n_in > 1 && s_in < D) return false;
+  if (n_out > 1 && s_out < (n_in > 1 ? s_in * n_in : (int64_t)D)) return false;
+  return true;
+}
+
 ffa_status check_shape(const ffa_shape* s) {
   if (!s) return FFA_ERR_INVALID_ARGUMENT;
   if (s->seqlen_q < 0 || s->seqlen_k < 0 || s->num_heads_q < 1 || s->num_heads_kv < 1)
@@ -219,7 +238,8 @@ FFA_API ffa_status ffa_fwd_grouped(const ffa_shape* shape, ffa_tensor_in q, ffa_
   if (!check_tensor(q.ptr, q.token_stride, q.head_stride, Tq, Hq, D) ||
       !check_tensor(o.ptr, o.token_stride, o.head_stride, Tq, Hq, D) ||
       !check_tensor(k.ptr, k.token_stride, k.head_stride, Tk, Hkv, D) ||
-      !check_tensor(v.ptr, v.token_stride, v.head_stride, Tk, Hkv, D))
+      !check_tensor(v.ptr, v.token_stride, v.head_stride, Tk, Hkv, D) ||
+      !rows_disjoint(o.token_stride, o.head_stride, Tq, Hq, D))
     return FFA_ERR_INVALID_ARGUMENT;
   if (Tq > 0 && (!lse || !aligned(lse, 16))) return FFA_ERR_INVALID_ARGUMENT;
   FwdArgs a;
@@ -308,7 +328,10 @@ FFA_API ffa_status ffa_bwd_grouped(const ffa_shape* shape, ffa_tensor_in q, ffa_
       !check_tensor(k.ptr, k.token_stride, k.head_stride, Tk, Hkv, D) ||
       !check_tensor(v.ptr, v.token_stride, v.head_stride, Tk, Hkv, D) ||
       !check_tensor(dk.ptr, dk.token_stride, dk.head_stride, Tk, Hkv, D) ||
-      !check_tensor(dv.ptr, dv.token_stride, dv.head_stride, Tk, Hkv, D))
+      !check_tensor(dv.ptr, dv.token_stride, dv.head_stride, Tk, Hkv, D) ||
+      !rows_disjoint(dq.token_stride, dq.head_stride, Tq, Hq, D) ||
+      !rows_disjoint(dk.token_stride, dk.head_stride, Tk, Hkv, D) ||
+      !rows_disjoint(dv.token_stride, dv.head_stride, Tk, Hkv, D))
     return FFA_ERR_INVALID_ARGUMENT;
   if (Tq > 0 && (!lse || !aligned(lse, 16))) return FFA_ERR_INVALID_ARGUMENT;
   BwdArgs a;

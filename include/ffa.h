@@ -24,6 +24,13 @@
  *  - Tensors are token-major ("THD"): q, o, dout, dq are [seqlen_q][num_heads_q][head_dim],
  *    k, v, dk, dv are [seqlen_k][num_heads_kv][head_dim], all bf16, with the
  *    last dimension contiguous and arbitrary token/head strides (in elements).
+ *    The rows of an output (one per token and head) must not share elements:
+ *    with its axes of more than one element ordered by stride, the inner
+ *    stride is at least head_dim and the outer one at least the inner stride
+ *    times the inner extent (views into one packed tensor qualify).  Outputs
+ *    must not share elements with each other or with the inputs (accumulate
+ *    mode reads and writes the same o and lse); the library checks the first
+ *    rule, not the second.
  *    Query head h reads key/value head h / (num_heads_q / num_heads_kv).
  *  - lse is fp32 [num_heads_q][seqlen_q], natural log, including the softmax
  *    scale: lse_i = ln sum_{j valid} exp(scale * q_i . k_j).
@@ -93,9 +100,9 @@ typedef struct {
 } ffa_tensor_in;
 
 typedef struct {
-  void* ptr;
-  int64_t token_stride;
-  int64_t head_stride;
+  void* ptr;             /* device, 16-byte aligned; strides as for inputs,  */
+  int64_t token_stride;  /* and its (token, head) rows must not overlap      */
+  int64_t head_stride;   /* (FFA_ERR_INVALID_ARGUMENT otherwise)             */
 } ffa_tensor_out;
 
 typedef struct {

@@ -113,10 +113,43 @@ def test_host_validation_returns_before_enqueue():
                         0x100000, ws.value, 7, 4, None) == 1
     assert L.ffa_bwd_ex(P(_shape()), good, good, good, good, lse, good, meta, goodo, goodo, goodo,
                         0x100000, ws.value - 1, 7, 1, None) == 3
+    # output rows that share elements (two workgroups would race on them):
+    # an expanded head axis, token and head strides equal, heads reaching
+    # into the next token; views into one packed [T][3 H][D] tensor and a
+    # head-major [H][T][D] layout pass
+    assert L.ffa_fwd(P(_shape()), good, good, good, meta, ffa.TensorOut(0x1000, 128, 0), lse, None) == 1
+    assert L.ffa_fwd(P(_shape()), good, good, good, meta, ffa.TensorOut(0x1000, 64, 64), lse, None) == 1
+    assert L.ffa_fwd(P(_shape(Hq=4)), good, good, good, meta, goodo, lse, None) == 1
+    assert L.ffa_fwd(P(_shape(d=128)), good, good, good, meta, ffa.TensorOut(0x1000, 256, 64), lse, None) == 1
+    packed_q, packed_k = ffa.TensorOut(0x1000, 3 * 2 * 64, 64), ffa.TensorOut(0x1080, 3 * 2 * 64, 64)
+    head_major = ffa.TensorOut(0x1000, 64, 256 * 64)
+    assert L.ffa_bwd(P(_shape()), good, good, good, good, lse, good, meta, packed_q, packed_k, head_major,
+                     0x100000, ws.value - 1, None) == 3
+    assert L.ffa_bwd(P(_shape()), good, good, good, good, lse, good, meta, ffa.TensorOut(0x1000, 64, 128),
+                     goodo, goodo, 0x100000, ws.value, None) == 1
+    assert L.ffa_bwd(P(_shape()), good, good, good, good, lse, good, meta, goodo,
+                     ffa.TensorOut(0x1000, 128, 0), goodo, 0x100000, ws.value, None) == 1
+    assert L.ffa_bwd(P(_shape()), good, good, good, good, lse, good, meta, goodo, goodo,
+                     ffa.TensorOut(0x1000, 64, 64), 0x100000, ws.value, None) == 1
+    # one token or one head: only head_dim matters along the other axis (each
+    # call is given one byte less workspace than its shape needs, so that
+    # passing the checks returns 3 and enqueues nothing)
+    def ws_short(sh):
+        need = ctypes.c_size_t()
+        assert L.ffa_bwd_workspace_size(P(sh), P(need)) == 0 and need.value > 0
+        return need.value - 1
+    sh1 = _shape(Tq=1)
+    assert L.ffa_bwd(P(sh1), good, good, good, good, lse, good, meta, ffa.TensorOut(0x1000, 64, 64),
+                     goodo, goodo, 0x100000, ws_short(sh1), None) == 3
+    sh1 = _shape(Hq=1, Hkv=1)
+    flat = ffa.TensorOut(0x1000, 64, 0)
+    assert L.ffa_bwd(P(sh1), good, good, good, good, lse, good, meta, flat, flat, flat,
+                     0x100000, ws_short(sh1), None) == 3
     # grouped calls: group count, order, coverage of the kv heads, alignment
     Metas = ctypes.c_void_p * 3
     Ends = ctypes.c_int32 * 3
     sh = _shape(Hq=4, Hkv=2)
+    goodo = ffa.TensorOut(0x1000, 256, 64)    # four query heads per token
     ok_m, ok_e = Metas(0x10000, 0x20000, 0), Ends(1, 2, 0)
     assert L.ffa_fwd_grouped(P(sh), good, good, good, 0, ok_m, ok_e, goodo, lse, 0, None) == 1
     assert L.ffa_fwd_grouped(P(sh), good, good, good, 9, ok_m, ok_e, goodo, lse, 0, None) == 1
