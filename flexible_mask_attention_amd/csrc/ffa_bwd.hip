@@ -303,7 +303,7 @@ __global__ __launch_bounds__(NT, 3) __attribute__((amdgpu_waves_per_eu(3, 3))) v
   auto tile_of = [&](int t) { return t < nP ? pidx[t] : fidx[t - nP]; };
   auto issue_tile = [&](int tile, int half, int stage) {
     const int key0 = tile * BN_F + half * SK;
-    char* st = smem + stage * STAGE_B;
+    const uint32_t st = lds_addr(smem) + stage * STAGE_B;
     if (wid < 2) dm.load(kbase, a.k_ts, key0, a.Tk - key0, st);
     else dm.load(vbase, a.v_ts, key0, a.Tk - key0, st + TILE_B);
   };

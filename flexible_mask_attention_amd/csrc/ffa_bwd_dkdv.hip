@@ -213,7 +213,7 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   dg_dma.init(wid, lane, a.do_ts);
   auto issue_tile = [&](int u, int m, int stage) {
     const int hq = kvh * G + u % G;
-    char* st = smem + stage * STAGE_B;
+    const uint32_t st = lds_addr(smem) + stage * STAGE_B;
     const int vr = a.Tq - m * BM_B;
     dq_dma.load(a.q + (int64_t)hq * a.q_hs, a.q_ts, m * BM_B, vr, st);
     dg_dma.load(a.dout + (int64_t)hq * a.do_hs, a.do_ts, m * BM_B, vr, st + TILE_B);

@@ -106,7 +106,7 @@ void ffa_fwd_kernel(FwdArgs a) {
   auto tile_of = [&](int t) { return t < nF ? fidx[t] : pidx[t - nF]; };
   auto issue_tile = [&](int tile, int half, int stage) {
     const int key0 = tile * BN_F + half * SK;
-    char* st = smem + stage * STAGE_B;
+    const uint32_t st = lds_addr(smem) + stage * STAGE_B;
     if (wid < 2) dm.load(kbase, a.k_ts, key0, a.Tk - key0, st);
     else dm.load(vbase, a.v_ts, key0, a.Tk - key0, st + TILE_B);
   };

@@ -282,15 +282,18 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t num_bytes)
 // waits explicitly (wait_dma) before the barrier that publishes them.  m0 is
 // a register the compiler reserves and would not honour as a clobber; no
 // generated code of these kernels keeps a value in m0 across the statements.
-__device__ __forceinline__ void dma16(const i32x4& r, char* lds_base, uint32_t voff, uint32_t soff) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(size_t)((__attribute__((address_space(3))) char*)lds_base));
+// LDS byte address of a __shared__ array (taken from the array itself, so
+// the compiler needs no null check of a generic pointer)
+__device__ __forceinline__ uint32_t lds_addr(const char* shared_array) {
+  return (uint32_t)(size_t)((const __attribute__((address_space(3))) char*)shared_array);
+}
+__device__ __forceinline__ void dma16(const i32x4& r, uint32_t lds, uint32_t voff, uint32_t soff) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :: "s"(m0), "v"(voff), "s"(r), "s"(soff) : "memory");
 }
-__device__ __forceinline__ void dma4(const i32x4& r, char* lds_base, uint32_t voff) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(size_t)((__attribute__((address_space(3))) char*)lds_base));
+__device__ __forceinline__ void dma4(const i32x4& r, uint32_t lds, uint32_t voff) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                :: "s"(m0), "v"(voff), "s"(r) : "memory");
 }
@@ -327,7 +330,7 @@ struct TileDma {
   // rows [row_base, row_base + ROWS) of a tensor (base pointer of row 0 of the
   // head), valid_rows of them in bounds
   __device__ __forceinline__ void load(const __bf16* head_base, int64_t ts_elems, int row_base,
-                                       int valid_rows, char* lds_tile) const {
+                                       int valid_rows, uint32_t lds_tile) const {
     const __bf16* b = head_base + (int64_t)row_base * ts_elems;
     const int vr = valid_rows < 0 ? 0 : (valid_rows > ROWS ? ROWS : valid_rows);
     const i32x4 r = make_rsrc(b, (uint32_t)(vr * ts_elems * 2));
