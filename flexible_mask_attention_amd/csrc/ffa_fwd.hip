@@ -163,6 +163,7 @@ void ffa_fwd_kernel(FwdArgs a) {
       if (iv_reg) {
 #pragma unroll
         for (int si = 0; si < NI; ++si) {
+          if (si >= nS) break;   // uniform: most blocks have one or two slices
           const int lo = max(ilo[si], key0), hi = min(ihi[si], key0 + SK - 1);
           if (lo <= hi) mk |= bit_range32(lo - key0, hi - key0);
         }
