@@ -327,7 +327,7 @@ __global__ __launch_bounds__(NT, 3) __attribute__((amdgpu_waves_per_eu(3, 3))) v
     // bit per key.  A stage with no valid pair for any of the wave's rows is
     // skipped: it would add nothing.
     uint32_t w = ~0u;
-    bool live = true;
+    bool live = true, need_mask = false;
     if (masked) {
       uint64_t mk = 0;
       for (int si = 0; si < nS; ++si) {
@@ -339,6 +339,8 @@ __global__ __launch_bounds__(NT, 3) __attribute__((amdgpu_waves_per_eu(3, 3))) v
         if (lo <= hi) mk |= bit_range(lo - key0, hi - key0);
       }
       live = __ballot(mk != 0) != 0;
+      // a stage valid for every key and row of this wave needs no masking
+      need_mask = __ballot(static_cast<uint32_t>(mk) != ~0u) != 0;
       w = static_cast<uint32_t>(mk >> (4 * h32));
     }
 
@@ -368,7 +370,7 @@ __global__ __launch_bounds__(NT, 3) __attribute__((amdgpu_waves_per_eu(3, 3))) v
           pacc = mfma32(va, gop[k], pacc);
         }
       }
-      if (masked) {
+      if (need_mask) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           sacc[r] = keep_or_neg_inf(sacc[r], w, 8 * (r >> 2) + (r & 3));

@@ -347,7 +347,8 @@ __global__ __launch_bounds__(NT, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) v
           pacc = mfma32(ga, vop[k], pacc);
         }
       }
-      if (masked) {
+      // a half valid for every row and key of this wave needs no masking
+      if (masked && __ballot(((mask_keep >> (32 * qb)) & 0xffffffffull) != 0xffffffffull) != 0) {
         const uint32_t w = static_cast<uint32_t>((mask_keep >> (4 * h32)) >> (32 * qb));
 #pragma unroll
         for (int r = 0; r < 16; ++r)

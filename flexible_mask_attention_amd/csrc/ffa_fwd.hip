@@ -157,7 +157,7 @@ void ffa_fwd_kernel(FwdArgs a) {
     // one bit per key.  A stage with no valid pair for any of the wave's rows
     // (e.g. above a causal diagonal) is skipped: it would add nothing.
     uint32_t w = ~0u;
-    bool live = true;
+    bool live = true, need_mask = false;
     if (masked) {
       uint32_t mk = 0;
       if (iv_reg) {
@@ -177,6 +177,9 @@ void ffa_fwd_kernel(FwdArgs a) {
         }
       }
       live = __ballot(mk != 0) != 0;
+      // inside a diagonal block, a stage can be valid for every key and row
+      // of this wave (its rows lie below the diagonal): nothing to mask
+      need_mask = __ballot(mk != ~0u) != 0;
       w = mk >> (4 * h32);   // register r holds key 8(r/4) + 4*h32 + r%4
     }
 
@@ -190,7 +193,7 @@ void ffa_fwd_kernel(FwdArgs a) {
         __builtin_memcpy(&kop, &u4, 16);
         sacc = mfma32(kop, qop[k], sacc);
       }
-      if (masked) {
+      if (need_mask) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           sacc[r] = keep_or_neg_inf(sacc[r], w, 8 * (r >> 2) + (r & 3));
