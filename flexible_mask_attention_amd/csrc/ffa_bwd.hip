@@ -192,6 +192,7 @@ __global__ __launch_bounds__(NT, 3) __attribute__((amdgpu_waves_per_eu(3, 3))) v
   constexpr int QREG = KS - NQL;
   constexpr int GB = group_bytes<SK>();
   static_assert(2 * SK == 16 * (NT / 64), "K and V stage tiles are loaded by half of the waves each");
+  static_assert(SK == 32, "a Partial stage's key mask is one 32-bit word");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -329,19 +330,19 @@ __global__ __launch_bounds__(NT, 3) __attribute__((amdgpu_waves_per_eu(3, 3))) v
     uint32_t w = ~0u;
     bool live = true, need_mask = false;
     if (masked) {
-      uint64_t mk = 0;
+      uint32_t mk = 0;   // bit j: key key0 + j (SK = 32)
       for (int si = 0; si < nS; ++si) {
         const Slice sl = load_slice(mv.slices, sidx[si]);
         int lo, hi;
         row_interval(sl, qrow, lo, hi);
         lo = max(lo, key0);
         hi = min(hi, key0 + SK - 1);
-        if (lo <= hi) mk |= bit_range(lo - key0, hi - key0);
+        if (lo <= hi) mk |= bit_range32(lo - key0, hi - key0);
       }
       live = __ballot(mk != 0) != 0;
       // a stage valid for every key and row of this wave needs no masking
-      need_mask = __ballot(static_cast<uint32_t>(mk) != ~0u) != 0;
-      w = static_cast<uint32_t>(mk >> (4 * h32));
+      need_mask = __ballot(mk != ~0u) != 0;
+      w = mk >> (4 * h32);   // register r holds key 8(r/4) + 4*h32 + r%4
     }
 
     if (live) {
