@@ -10,11 +10,15 @@ Pins of the oracle:
     than the exhaustive optimum, reaches it where the optimum is known (equal
     areas; a causal sequence cut into 2 * cp chunks, where pairing chunk i with
     chunk n - 1 - i balances exactly), and a planted mistake (lightest-bucket
-    rule dropped) is caught.
+    rule dropped) is caught;
+  * the exhaustive optimum equals a plain enumeration of equal-count
+    labellings on small inputs and a worked example, and a search that drops
+    the equal-count rule is caught.
 Library checks: chunk areas and bucket choices identical to the oracle's; a
 rank's local slice table reproduces the global mask on its queries and the
 keys it receives exactly, and every valid key of those queries is received.
 """
+import itertools
 import random
 
 import numpy as np
@@ -89,6 +93,43 @@ def test_oracle_greedy_invariants_and_optimum():
             assert g == opt
     # equal areas: perfect balance
     assert dor.max_load([4] * 12, dor.greedy_dispatch([4] * 12, 4), 4) == 12
+
+
+def _brute_max_load(areas, cp):
+    """Min over every labelling of the chunks with cp buckets, each bucket
+    taking n / cp chunks, of the heaviest bucket."""
+    n, cap, best = len(areas), len(areas) // cp, None
+    for lab in itertools.product(range(cp), repeat=n):
+        if any(lab.count(b) != cap for b in range(cp)):
+            continue
+        m = max(sum(a for a, l in zip(areas, lab) if l == b) for b in range(cp))
+        best = m if best is None else min(best, m)
+    return best
+
+
+def test_oracle_best_max_load_vs_brute_force():
+    """The exhaustive search (recursive choice of each bucket's members) against
+    a plain enumeration of labellings, plus a worked example: six chunks
+    8, 7, 6, 5, 4, 3 into two buckets of three sum to 33, so the heavier bucket
+    holds at least 17, and {8, 6, 3} / {7, 5, 4} reaches it."""
+    assert dor.best_max_load([8, 7, 6, 5, 4, 3], 2) == 17
+    rng = random.Random(11)
+    for _ in range(80):
+        cp = rng.choice([2, 3])
+        n = cp * rng.choice([1, 2]) if cp == 3 else cp * rng.choice([1, 2, 3, 4])
+        areas = [rng.randint(0, 30) for _ in range(n)]
+        assert dor.best_max_load(areas, cp) == _brute_max_load(areas, cp), (areas, cp)
+
+
+def test_oracle_best_max_load_pin_catches_dropped_count_rule(monkeypatch):
+    """An exhaustive search that forgets the equal-count rule (any subset per
+    bucket) reports a lower optimum on some input and fails the pin."""
+    def unconstrained(areas, cp):
+        return min(max(sum(a for a, l in zip(areas, lab) if l == b) for b in range(cp))
+                   for lab in itertools.product(range(cp), repeat=len(areas)))
+    monkeypatch.setattr(dor, "best_max_load", unconstrained)
+    with pytest.raises(AssertionError):
+        test_oracle_best_max_load_vs_brute_force()
 
 
 @pytest.mark.parametrize("cp,chunk", [(2, 64), (4, 32), (8, 16)])
